@@ -22,7 +22,8 @@
  *   oracle_route_topk     brute force by full stable sort; scipy softmax at
  *                         topk == E; topk == 1 gives weight exactly 1
  *   oracle_align_sort     Python sorted() brute force and segment invariants
- *   oracle_moe_forward    numpy float64 dense SwiGLU MLP (E = 1, topk = 1);
+ *   oracle_moe_forward    numpy float64 dense SwiGLU MLP with torch's bf16
+ *                         cast of the SwiGLU output (E = 1, topk = 1);
  *                         per-token dense reconstruction on tiny shapes;
  *                         routing independence with identical experts
  *   oracle_requant_int4g32 hand-derived closed-form code table (the e8m0
@@ -81,32 +82,32 @@ uint16_t oracle_f32_to_bf16_rne(float v) {
     return (uint16_t)(u >> 16);
 }
 
-/* Value of element (row, k) of a [rows, K] weight in either format.
+/* Row `row` of a [rows, K] weight in either format, into out[K].
  * MXFP4: e2m1(nibble) * 2^(e8m0 - 127), one scale per 32 along K
  *        ([P2] create_weights: mxfp4_block = 32; convert(): the f32 weight
  *        viewed as [.., K/32, 32] times the scale viewed as [.., K/32, 1]).
  * INT4G32: two's-complement nibble times its group's bf16 scale ([P1]
  *        Summary: int4 with groupwise bf16 scales, group 32). */
-static double weight_value(const uint8_t* w, const void* scale, int fmt,
-                           int K, int64_t row, int k) {
+static void dequant_row(const uint8_t* w, const void* scale, int fmt, int K, int64_t row,
+                        double* out) {
     const uint8_t* wrow = w + row * (int64_t)(K / 2);
-    int code = oracle_nibble(wrow, k);
-    int64_t si = row * (int64_t)(K / 32) + k / 32;
-    if (fmt == ORACLE_FMT_MXFP4) {
-        const uint8_t* s = (const uint8_t*)scale;
-        return oracle_e2m1_value(code) * oracle_e8m0_value(s[si]);
-    } else {
-        const uint16_t* s = (const uint16_t*)scale;
-        int q = code >= 8 ? code - 16 : code;
-        return (double)q * oracle_bf16_value(s[si]);
+    for (int g = 0; g < K / 32; ++g) {
+        int64_t si = row * (int64_t)(K / 32) + g;
+        double s = fmt == ORACLE_FMT_MXFP4 ? oracle_e8m0_value(((const uint8_t*)scale)[si])
+                                           : oracle_bf16_value(((const uint16_t*)scale)[si]);
+        for (int i = 0; i < 32; ++i) {
+            int k = g * 32 + i;
+            int code = oracle_nibble(wrow, k);
+            double v = fmt == ORACLE_FMT_MXFP4 ? oracle_e2m1_value(code)
+                                               : (double)(code >= 8 ? code - 16 : code);
+            out[k] = v * s;
+        }
     }
 }
 
 void oracle_dequant(const uint8_t* w, const void* scale, int fmt,
                     int rows, int K, double* out) {
-    for (int64_t r = 0; r < rows; ++r)
-        for (int k = 0; k < K; ++k)
-            out[r * K + k] = weight_value(w, scale, fmt, K, r, k);
+    for (int64_t r = 0; r < rows; ++r) dequant_row(w, scale, fmt, K, r, out + r * K);
 }
 
 /* --------------------------------------------------------------- routing -- */
@@ -195,29 +196,51 @@ static double silu(double z) { return z / (1.0 + exp(-z)); }
 
 /* One pair (token t, expert e): gate/up projection against w13 (rows [0, I)
  * gate, rows [I, 2I) up -- the fused gate_up_proj of [P2] create_weights),
- * SwiGLU silu(gate) * up, then the down projection against w2. y[H] out. */
+ * SwiGLU silu(gate) * up rounded to bf16, then the down projection against
+ * w2. y[H] out.
+ * Every dot product is summed in ascending k. */
 static void expert_mlp(const uint16_t* xt, const uint8_t* w13, const void* w13_scale,
                        const uint8_t* w2, const void* w2_scale, int fmt,
                        int e, int H, int I, double* hbuf, double* y) {
     int64_t r13 = (int64_t)e * 2 * I; /* first w13 row of expert e */
     int64_t r2 = (int64_t)e * H;      /* first w2 row of expert e */
-#pragma omp parallel for schedule(static)
-    for (int i = 0; i < I; ++i) {
-        double g = 0.0, u = 0.0;
-        for (int k = 0; k < H; ++k) {
-            double xv = oracle_bf16_value(xt[k]);
-            g += weight_value(w13, w13_scale, fmt, H, r13 + i, k) * xv;
-            u += weight_value(w13, w13_scale, fmt, H, r13 + I + i, k) * xv;
+    double* xv = (double*)malloc(sizeof(double) * (size_t)H);
+    for (int k = 0; k < H; ++k) xv[k] = oracle_bf16_value(xt[k]);
+#pragma omp parallel
+    {
+        double* wg = (double*)malloc(sizeof(double) * (size_t)H);
+        double* wu = (double*)malloc(sizeof(double) * (size_t)H);
+#pragma omp for schedule(static)
+        for (int i = 0; i < I; ++i) {
+            dequant_row(w13, w13_scale, fmt, H, r13 + i, wg);
+            dequant_row(w13, w13_scale, fmt, H, r13 + I + i, wu);
+            double g = 0.0, u = 0.0;
+            for (int k = 0; k < H; ++k) {
+                g += wg[k] * xv[k];
+                u += wu[k] * xv[k];
+            }
+            /* A16W4: both grouped GEMMs take bf16 activations, so the
+             * SwiGLU output enters the down projection as bf16 ([P1]
+             * Summary: the BF16 x packed-int4 path; [P2] EMULATION comment:
+             * bf16 activations, only the weights dequantized). */
+            hbuf[i] = oracle_bf16_value(oracle_f32_to_bf16_rne((float)(silu(g) * u)));
         }
-        hbuf[i] = silu(g) * u;
+        free(wu);
+        free(wg);
     }
-#pragma omp parallel for schedule(static)
-    for (int n = 0; n < H; ++n) {
-        double acc = 0.0;
-        for (int i = 0; i < I; ++i)
-            acc += weight_value(w2, w2_scale, fmt, I, r2 + n, i) * hbuf[i];
-        y[n] = acc;
+#pragma omp parallel
+    {
+        double* wd = (double*)malloc(sizeof(double) * (size_t)I);
+#pragma omp for schedule(static)
+        for (int n = 0; n < H; ++n) {
+            dequant_row(w2, w2_scale, fmt, I, r2 + n, wd);
+            double acc = 0.0;
+            for (int i = 0; i < I; ++i) acc += wd[i] * hbuf[i];
+            y[n] = acc;
+        }
+        free(wd);
     }
+    free(xv);
 }
 
 /* out[t] = sum over the token's topk slots (ascending) of weight * expert

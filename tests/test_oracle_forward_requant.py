@@ -2,9 +2,11 @@
 
 Forward: W4A16 semantics (get_fused_moe_quant_config on the vLLM mxfp4 API
 page: bf16 activations, weights dequantized), fused gate_up rows [0, I) gate
-and [I, 2I) up (create_weights), SwiGLU, down projection, router weights
-applied at the combine (apply()). Pins: numpy float64 matmuls over weights
-decoded by tests/decode_ref.py, scipy's expit for the sigmoid.
+and [I, 2I) up (create_weights), SwiGLU whose output enters the down GEMM as
+bf16 (the BF16 x packed-int4 path of the MXFP4-to-int4 pull request), down
+projection, router weights applied at the combine (apply()). Pins: numpy
+float64 matmuls over weights decoded by tests/decode_ref.py, scipy's expit
+for the sigmoid, torch's bf16 cast for the activation rounding.
 
 Requant: convert() in Mxfp4MoEMethod._setup_kernel_k3_situ_gfx942 (decode,
 scale, bf16 cast, per-1x32 int4 quant, pack); pinned by the closed-form code
@@ -20,10 +22,14 @@ from tests.decode_ref import (E2M1_TABLE, bf16_bits_to_f64, dequant_int4g32, deq
                               unpack_nibbles)
 
 
+def _bf16(a):
+    return torch.from_numpy(np.asarray(a, dtype=np.float32)).to(torch.bfloat16).double().numpy()
+
+
 def _mlp(x, w13d, w2d, I):
     g = w13d[:I] @ x
     u = w13d[I:] @ x
-    h = g * expit(g) * u
+    h = _bf16(g * expit(g) * u)  # the down GEMM's activation operand is bf16 (A16W4)
     return w2d @ h
 
 
