@@ -1,0 +1,305 @@
+#!/usr/bin/env python3
+"""Benchmark of the A16W4 MoE layer on one MI355X.
+
+A step is one pass of the whole layer over one batch: softmax top-k routing,
+align/sort, grouped gate_up GEMM + SwiGLU, grouped down GEMM and the weighted
+combine, with every input already resident in HBM. Steps rotate over
+--sets independent weight sets and routings (like consecutive layers of a
+model), so weights are streamed from HBM rather than served by the 256 MB
+Infinity Cache. Default workload: decode, tokens=1 at the production
+expert-parallel shape (H=3584, I=3072, 112 local experts, topk=15) with MXFP4
+weights.
+
+Prints one JSON line. `value` is tokens/s of the timed steps (HIP-graph
+replay of the step, as served under graph capture); `roofline` is the
+dominant kernel (the gate_up stage) timed with HIP events on the launch
+stream in a second, eager pass; `cpu_baseline` is the CPU oracle on a bounded
+sample of the same workload.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE layer tokens/s + achieved HBM GB/s (decode) / MFMA % (prefill) at H3584,E112"
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="decode_t1",
+                    help="decode_t1 (default), decode_t{4,7,16,32}, skewed_t{4,7,16,32}, "
+                         "prefill_t1024, int4_t16")
+    ap.add_argument("--sets", type=int, default=8, help="independent weight sets / routings")
+    ap.add_argument("--eager", action="store_true", help="time eager launches, not graph replay")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="run only a plain 1 GiB device copy (HBM counter calibration)")
+    return ap.parse_args()
+
+
+def copy_probe():
+    import torch
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").random_(0, 255)
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n, "launches": 5}))
+
+
+class Layer:
+    """Device buffers of one weight set + routing, and the launches of a step."""
+
+    def __init__(self, moe, spec, T, fmt, seed, host=None, int4=False):
+        import numpy as np
+        import torch
+        self.moe, self.T, self.fmt = moe, T, fmt
+        s = spec
+        H, I, E, k = s.H, s.I, s.E, s.topk
+        self.H, self.I, self.E, self.k = H, I, E, k
+        dev = torch.device("cuda")
+        if host is not None:
+            self.x = torch.from_numpy(host.x.view(np.int16)).view(torch.bfloat16).to(dev)
+            self.logits = torch.from_numpy(host.logits).to(dev)
+            w = [torch.from_numpy(a).to(dev) for a in (host.w13, host.w13_scale, host.w2, host.w2_scale)]
+        else:
+            g = torch.Generator(device=dev)
+            g.manual_seed(seed)
+            self.x = torch.randn((T, H), generator=g, device=dev).to(torch.bfloat16)
+            self.logits = torch.randn((T, E), generator=g, device=dev)
+            if s.hot:
+                hot = torch.randperm(E, generator=g, device=dev)[: s.hot]
+                self.logits[:, hot] += s.hot_bias
+            w = [torch.randint(0, 256, (E, 2 * I, H // 2), generator=g, device=dev, dtype=torch.uint8),
+                 torch.randint(s.scale_lo, s.scale_hi + 1, (E, 2 * I, H // 32), generator=g, device=dev,
+                               dtype=torch.uint8),
+                 torch.randint(0, 256, (E, H, I // 2), generator=g, device=dev, dtype=torch.uint8),
+                 torch.randint(s.scale_lo, s.scale_hi + 1, (E, H, I // 32), generator=g, device=dev,
+                               dtype=torch.uint8)]
+        if int4:
+            q13, s13 = moe.requantize_mxfp4_experts(w[0], w[1])
+            q2, s2 = moe.requantize_mxfp4_experts(w[2], w[3])
+            w = [q13, s13, q2, s2]
+            torch.cuda.synchronize()
+        self.w13, self.w13s, self.w2, self.w2s = w
+        self.bm = moe.moe_default_block_m(T, k, E)
+        cap = moe.moe_align_sort_capacity(T, k, E, self.bm)
+        self.ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+        self.wts = torch.empty((T, k), dtype=torch.float32, device=dev)
+        self.sort = (torch.empty(cap, dtype=torch.int32, device=dev),
+                     torch.empty(cap // self.bm, dtype=torch.int32, device=dev),
+                     torch.empty(E + 1, dtype=torch.int32, device=dev),
+                     torch.empty(1, dtype=torch.int32, device=dev))
+        self.out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+        self.ws = torch.empty(moe.moe_a16w4_workspace_size(T, H, I, E, k, self.bm), dtype=torch.uint8,
+                              device=dev)
+
+    def route_sort(self):
+        self.moe.moe_route_topk(self.logits, self.k, True, self.ids, self.wts)
+        self.moe.moe_align_sort(self.ids, self.E, self.bm, out=self.sort)
+
+    def forward(self, stages=7):
+        s, be, _, npp = self.sort
+        self.moe.moe_a16w4_forward(self.x, self.w13, self.w13s, self.w2, self.w2s, self.ids, self.wts,
+                                   s, be, npp, self.bm, fmt=self.fmt, out=self.out, workspace=self.ws,
+                                   stages=stages)
+
+    def step(self):
+        self.route_sort()
+        self.forward()
+
+    def distinct_experts(self):
+        import torch
+        return int(torch.unique(self.ids).numel())
+
+
+def weight_bytes_per_expert(H, I, fmt):
+    sb = 1 if fmt == 0 else 2
+    w13 = 2 * I * (H // 2) + 2 * I * (H // 32) * sb
+    w2 = H * (I // 2) + H * (I // 32) * sb
+    return w13, w2
+
+
+def cpu_baseline(wl, spec, seconds, fmt_name):
+    """The CPU oracle (test infrastructure) timed on this host, tokens/s."""
+    import numpy as np
+    import oracle
+    T = wl.x.shape[0]
+    n_tok = T if T <= 4 else 2
+    tokens = np.arange(n_tok, dtype=np.int32)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        ids, w = oracle.route_topk(wl.logits, spec.topk)
+        oracle.align_sort(ids, spec.E, 16)
+        oracle.moe_forward(wl.x, wl.w13, wl.w13_scale, wl.w2, wl.w2_scale, oracle.FMT_MXFP4, ids, w,
+                           I=spec.I, tokens=tokens if n_tok < T else None)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": round(reps * n_tok / el, 4), "unit": "tokens/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{reps} x (route + align/sort of all {T} tokens + forward of {n_tok} token(s)) of "
+                      f"the {fmt_name} workload, weight set 0, {el:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the layer here is one "
+              "expert-parallel rank's share and this build has no multi-GPU path.", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_probe:
+        copy_probe()
+        return
+
+    import numpy as np
+    import torch
+
+    import mxfp4_grouped_gemm_amd as moe
+    import synth
+
+    specs = synth.specs()
+    if args.workload not in specs or args.workload == "tiny":
+        raise SystemExit(f"unknown workload {args.workload}")
+    spec = specs[args.workload]
+    int4 = args.workload.startswith("int4")
+    fmt = moe.MOE_W_INT4G32 if int4 else moe.MOE_W_MXFP4
+    T = spec.T
+    host = synth.make(spec)
+    layers = [Layer(moe, spec, T, fmt, seed=1000 + i, host=host if i == 0 else None, int4=int4)
+              for i in range(args.sets)]
+    torch.cuda.synchronize()
+    R = len(layers)
+
+    # routing of each set (for the algorithmic byte counts)
+    for L in layers:
+        L.route_sort()
+    torch.cuda.synchronize()
+    distinct = [L.distinct_experts() for L in layers]
+
+    # ---- headline: graph replay (or eager) of whole steps
+    graphs = None
+    if not args.eager:
+        graphs = []
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for L in layers:  # warm the launch path once outside capture
+                L.step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        for L in layers:
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                L.step()
+            graphs.append(g)
+        torch.cuda.synchronize()
+
+    def run(i):
+        if graphs is not None:
+            graphs[i % R].replay()
+        else:
+            layers[i % R].step()
+
+    for i in range(args.warmup):
+        run(i)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(args.steps):
+        run(i)
+    end.record()
+    torch.cuda.synchronize()
+    ms_per_step = start.elapsed_time(end) / args.steps
+
+    # ---- per-stage timing (eager, events on the launch stream)
+    nst = max(args.steps, 8)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(nst)]
+    for i in range(min(args.warmup, 4)):
+        layers[i % R].step()
+    torch.cuda.synchronize()
+    for i in range(nst):
+        L, e = layers[i % R], ev[i]
+        e[0].record()
+        L.route_sort()
+        e[1].record()
+        L.forward(moe.MOE_STAGE_GATE_UP)
+        e[2].record()
+        L.forward(moe.MOE_STAGE_DOWN)
+        e[3].record()
+        L.forward(moe.MOE_STAGE_COMBINE)
+        e[4].record()
+    torch.cuda.synchronize()
+    stage_ms = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(4)] for e in ev])
+    stage_avg = stage_ms.mean(axis=0)
+    eager_ms = float(stage_ms.sum(axis=1).mean())
+
+    H, I, E, k = spec.H, spec.I, spec.E, spec.topk
+    P = T * k
+    w13_b, w2_b = weight_bytes_per_expert(H, I, fmt)
+    d_avg = float(np.mean([distinct[i % R] for i in range(nst)]))
+    act_bytes_1 = T * H * 2 + P * I * 2            # x read, h written
+    stage1_bytes = d_avg * w13_b + act_bytes_1
+    layer_bytes = d_avg * (w13_b + w2_b) + 2 * T * H * 2 + T * E * 4
+    stage1_flops = 2.0 * P * (2 * I) * H
+    layer_flops = 2.0 * P * 3 * I * H
+    s1_sec = stage_avg[1] * 1e-3
+    if spec.T >= 256:
+        ach = stage1_flops / s1_sec / 1e12
+        roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": None}
+    else:
+        ach = stage1_bytes / s1_sec / 1e9
+        roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": None}
+    roof["kernel"] = "stage1_stream_kernel (grouped gate_up GEMM + SwiGLU)"
+    roof["avg_us"] = round(stage_avg[1] * 1e3, 2)
+    roof["algorithmic_per_launch"] = (round(stage1_flops) if roof["bound"] == "mfma"
+                                      else round(stage1_bytes))
+
+    value = T / (ms_per_step * 1e-3)
+    line = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": args.workload, "tokens": T, "H": H, "I": I, "experts": E, "topk": k,
+                   "weights": "int4_g32" if int4 else "mxfp4", "block_m": layers[0].bm,
+                   "weight_sets": R, "timing": "eager" if args.eager else "hip_graph_replay",
+                   "distinct_experts_avg": round(d_avg, 2)},
+        "layer_hbm_gbps": round(layer_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+        "layer_tflops": round(layer_flops / (ms_per_step * 1e-3) / 1e12, 2),
+        "eager_ms_per_step": round(eager_ms, 5),
+        "stage_us": {"route_sort": round(stage_avg[0] * 1e3, 2), "gate_up": round(stage_avg[1] * 1e3, 2),
+                     "down": round(stage_avg[2] * 1e3, 2), "combine": round(stage_avg[3] * 1e3, 2)},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(host, spec, args.cpu_seconds,
+                                            "int4_g32" if int4 else "MXFP4")
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,188 @@
+/*
+ * moe_a16w4 -- fused mixture-of-experts layer with bf16 activations and
+ * 4-bit expert weights (A16W4) for AMD Instinct MI355X (gfx950).
+ *
+ * The layer, per token t with router logits l[t, :] and activation x[t, :]:
+ *   1. route: the topk experts with the largest logits, weighted by their
+ *      softmax probabilities renormalised over the chosen k;
+ *   2. align/sort: the (token, slot) pairs grouped by expert;
+ *   3. per pair (t, j) with expert e: gate/up = W13[e] . x[t]
+ *      (rows [0, I) gate, rows [I, 2I) up), h = silu(gate) * up,
+ *      y = W2[e] . h;
+ *   4. out[t] = sum_j weight[t, j] * y(t, j).
+ *
+ * Sources: the vLLM API page of the mxfp4 quantization module, class
+ * Mxfp4MoEMethod (create_weights: the weight and scale tensor shapes;
+ * apply / apply_monolithic: forward with precomputed or in-kernel routing;
+ * _setup_kernel_k3_situ_gfx942: the MXFP4 -> int4 requantization), and the
+ * vLLM pull request "[ROCm][Kimi-K3] Add opt-in gfx942 MXFP4-to-int4
+ * conversion" (Summary, Changes: the int4_per_group_32 format, conversion
+ * eight experts at a time, fail-closed activation check).
+ *
+ * Conventions for every call:
+ *   - Pointers are caller-owned device memory unless stated otherwise; the
+ *     library never allocates device memory.
+ *   - `stream` is a hipStream_t (NULL = the default stream). Work is
+ *     enqueued asynchronously; no call synchronises the host, so a sequence
+ *     of calls may be captured into a HIP graph.
+ *   - Arguments are validated before anything is enqueued; on any error
+ *     nothing is launched and moe_last_error() describes the problem.
+ *   - bf16 values travel as uint16_t bit patterns.
+ *   - Data held in device memory is not validated (it cannot be read without
+ *     a host synchronisation); out-of-contract device data gives unspecified
+ *     results but never out-of-bounds accesses, except where noted.
+ */
+#ifndef MOE_A16W4_H
+#define MOE_A16W4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = 1, /* a size, pointer or range is invalid */
+    MOE_ERR_UNSUPPORTED = 2, /* valid request outside what is implemented */
+    MOE_ERR_HIP = 3          /* the HIP runtime reported an error at launch */
+} moe_status;
+
+/* Weight formats. MXFP4 is the checkpoint format (create_weights on the
+ * mxfp4 API page): e2m1 nibbles packed two per byte along K (even k in the
+ * low nibble) with one e8m0 byte per 32 elements along K. INT4G32 is the
+ * opt-in int4_per_group_32 format of the MXFP4-to-int4 pull request:
+ * two's-complement int4 nibbles with the same packing and one bf16 scale per
+ * 32 elements along K. */
+typedef enum { MOE_W_MXFP4 = 0, MOE_W_INT4G32 = 1 } moe_wfmt;
+
+/* Gated activations. Only SwiGLU, silu(gate) * up, is implemented; any other
+ * value fails closed with MOE_ERR_UNSUPPORTED rather than silently computing
+ * SwiGLU (the pull request's Changes: fail closed unless the kernel honours
+ * the requested activation). */
+typedef enum { MOE_ACT_SWIGLU = 0 } moe_act;
+
+/* Message for the last non-OK status returned on the calling thread
+ * (a static, thread-local string; never NULL). */
+const char* moe_last_error(void);
+
+/* Softmax top-k routing (the routing inside apply_monolithic on the mxfp4
+ * API page; the pages do not print the rule, this is plain softmax top-k).
+ *   logits        fp32 [T, E], row-major.
+ *   topk_ids      out int32 [T, topk]: expert indices in descending logit
+ *                 order; equal logits rank the lower index first.
+ *   topk_weights  out fp32 [T, topk]: softmax probabilities of the chosen
+ *                 experts, renormalised to sum 1 when renormalize != 0.
+ * Limits: T >= 0 (T == 0 is a no-op), 1 <= E <= 1024, 1 <= topk <= min(E, 64).
+ * NaN logits give unspecified (in-range) ids. */
+moe_status moe_route_topk(const float* logits, int T, int E, int topk, int renormalize,
+                          int32_t* topk_ids, float* topk_weights, void* stream);
+
+/* Rows of sorted_ids needed for T*topk pairs over E experts when every
+ * expert segment is padded to a multiple of block_m:
+ * roundup(P + min(E, P) * (block_m - 1), block_m), P = T*topk.
+ * Returns -1 for invalid arguments. */
+int64_t moe_align_sort_capacity(int T, int topk, int E, int block_m);
+
+/* Block size the forward works best with for this token count
+ * (one of 16, 32, 64, 128). */
+int moe_default_block_m(int T, int topk, int E);
+
+/* Group the P = T*topk (token, slot) pairs by expert for the grouped GEMMs
+ * of the two-stage MoE. Pair p = t*topk + j.
+ *   topk_ids        int32 [T, topk]; ids within a token must be distinct
+ *                   and in [0, E) -- pairs with an id outside [0, E) are
+ *                   dropped (not listed).
+ *   block_m         16, 32, 64, 128 or 256.
+ *   sorted_ids      out int32 [cap] (cap = moe_align_sort_capacity): for
+ *                   each expert in ascending order, its pairs in ascending p,
+ *                   padded to a multiple of block_m with the sentinel P;
+ *                   rows past the last segment are P as well.
+ *   block_expert    out int32 [cap / block_m]: expert of each block, -1 for
+ *                   blocks past the last segment.
+ *   expert_offsets  out int32 [E + 1]: start row of each expert's padded
+ *                   segment; expert_offsets[E] == *num_post_pad.
+ *   num_post_pad    out int32 [1]: rows in use.
+ * The result is deterministic (no dependence on atomic ordering).
+ * Limits: E <= 1024, T*topk < 2^31 - cap. */
+moe_status moe_align_sort(const int32_t* topk_ids, int T, int topk, int E, int block_m,
+                          int32_t* sorted_ids, int32_t* block_expert, int32_t* expert_offsets,
+                          int32_t* num_post_pad, void* stream);
+
+/* Bytes of device workspace moe_a16w4_forward needs (256-byte aligned
+ * start required). Returns -1 for invalid arguments. */
+int64_t moe_a16w4_workspace_size(int T, int H, int I, int E, int topk, int block_m);
+
+/* Fused MoE forward with precomputed routing (apply() on the mxfp4 API
+ * page): grouped gate_up GEMM with the weights dequantized in registers,
+ * SwiGLU, grouped down GEMM, top-k weighted combine.
+ *   x             bf16 [T, H].
+ *   w13           uint8 [E, 2I, H/2] packed 4-bit weights (gate rows [0, I),
+ *                 up rows [I, 2I)); w13_scale [E, 2I, H/32]: uint8 e8m0 for
+ *                 MXFP4, uint16 bf16 for INT4G32.
+ *   w2            uint8 [E, H, I/2]; w2_scale [E, H, I/32] (same typing).
+ *   topk_ids, topk_weights   int32 / fp32 [T, topk] (router weights are
+ *                 applied at the combine).
+ *   sorted_ids, block_expert, num_post_pad   moe_align_sort's output for
+ *                 the same topk_ids and block_m.
+ *   out           bf16 [T, H].
+ *   workspace     device memory of moe_a16w4_workspace_size bytes.
+ * Requirements: H % 32 == 0, I % 32 == 0, H >= 32, I >= 32, E >= 1,
+ *   1 <= topk <= E, block_m in {16, 32, 64, 128, 256}; all pointers
+ *   16-byte aligned (workspace 256-byte aligned).
+ * MXFP4 e8m0 bytes must be in [0, 254]; weights whose value overflows bf16
+ * give unspecified results. */
+moe_status moe_a16w4_forward(const uint16_t* x, const uint8_t* w13, const void* w13_scale,
+                             const uint8_t* w2, const void* w2_scale, moe_wfmt fmt, moe_act act,
+                             const int32_t* topk_ids, const float* topk_weights,
+                             const int32_t* sorted_ids, const int32_t* block_expert,
+                             const int32_t* num_post_pad, int T, int H, int I, int E, int topk,
+                             int block_m, uint16_t* out, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+/* The forward split into its launches, for callers that schedule or time
+ * them separately (the modular-kernel stages of the pages). Bits of
+ * `stages`: MOE_STAGE_GATE_UP (grouped gate_up GEMM + SwiGLU into the
+ * workspace), MOE_STAGE_DOWN (grouped down GEMM from the workspace into the
+ * workspace), MOE_STAGE_COMBINE (weighted combine from the workspace into
+ * out). Enabled stages run in that order on `stream`; a stage reads what
+ * the previous stage wrote into the same workspace for the same arguments.
+ * moe_a16w4_forward == moe_a16w4_forward_stages with MOE_STAGE_ALL. Same
+ * arguments, requirements and errors as moe_a16w4_forward; stages == 0 or
+ * unknown bits give MOE_ERR_INVALID_ARG. */
+#define MOE_STAGE_GATE_UP 1u
+#define MOE_STAGE_DOWN 2u
+#define MOE_STAGE_COMBINE 4u
+#define MOE_STAGE_ALL 7u
+moe_status moe_a16w4_forward_stages(const uint16_t* x, const uint8_t* w13, const void* w13_scale,
+                                    const uint8_t* w2, const void* w2_scale, moe_wfmt fmt,
+                                    moe_act act, const int32_t* topk_ids,
+                                    const float* topk_weights, const int32_t* sorted_ids,
+                                    const int32_t* block_expert, const int32_t* num_post_pad, int T,
+                                    int H, int I, int E, int topk, int block_m, uint16_t* out,
+                                    void* workspace, size_t workspace_bytes, unsigned stages,
+                                    void* stream);
+
+/* MXFP4 -> int4 per-group-32 requantization of experts [expert_lo,
+ * expert_hi) of a [E, N, K] weight (convert() in
+ * Mxfp4MoEMethod._setup_kernel_k3_situ_gfx942; the pull request converts
+ * eight experts per call into preallocated outputs). Per 32-group along K:
+ * v = bf16(e2m1 * 2^(e8m0 - 127)); scale = bf16(amax(|v|) / 7) computed in
+ * fp32; code = clamp(round_half_even(v / scale), -8, 7) with an IEEE fp32
+ * divide (an all-zero group gives scale 0 and codes 0); codes packed two per
+ * byte, even k in the low nibble.
+ *   w, scale_e8m0   uint8 [E, N, K/2] and [E, N, K/32] (MXFP4).
+ *   w_int4          out uint8 [E, N, K/2]; scale_bf16 out uint16 [E, N, K/32].
+ *                   Only experts in [expert_lo, expert_hi) are written; the
+ *                   library uses no scratch memory beyond these outputs.
+ * Requirements: K % 32 == 0, N >= 1, 0 <= expert_lo <= expert_hi <= E;
+ * pointers 16-byte aligned. Lossy by construction. */
+moe_status mxfp4_to_int4g32_requant(const uint8_t* w, const uint8_t* scale_e8m0, int E, int N,
+                                    int K, int expert_lo, int expert_hi, uint8_t* w_int4,
+                                    uint16_t* scale_bf16, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_A16W4_H */

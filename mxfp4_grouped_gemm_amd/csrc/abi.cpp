@@ -1,0 +1,230 @@
+// C ABI of the A16W4 MoE library: argument validation, workspace layout and
+// kernel selection. Every check runs before anything is enqueued, so an
+// error leaves the stream untouched (the shape checks of
+// Mxfp4MoEMethod._setup_kernel and the fail-closed activation check of the
+// MXFP4-to-int4 pull request).
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/moe_a16w4.h"
+#include "launch.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "no error";
+
+moe_status fail(moe_status st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+moe_status hip_status(hipError_t e, const char* what) {
+    if (e == hipSuccess) return MOE_OK;
+    return fail(MOE_ERR_HIP, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool valid_bm(int bm) { return bm == 16 || bm == 32 || bm == 64 || bm == 128 || bm == 256; }
+
+// Block sizes the GEMM kernels are built for.
+bool forward_bm(int bm) { return bm == 16 || bm == 32 || bm == 64; }
+
+int64_t capacity(int T, int topk, int E, int bm) {
+    const int64_t P = (int64_t)T * topk;
+    const int64_t groups = P < E ? P : E;
+    const int64_t cap = P + groups * (bm - 1);
+    return (cap + bm - 1) / bm * bm;
+}
+
+int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
+
+struct WsLayout {
+    int64_t h_off, h_bytes, y_off, y_bytes, total;
+};
+
+WsLayout ws_layout(int T, int H, int I, int E, int topk, int bm) {
+    WsLayout L;
+    const int64_t cap = capacity(T, topk, E, bm);
+    L.h_off = 0;
+    L.h_bytes = align_up(cap * I * 2, 256);
+    L.y_off = L.h_off + L.h_bytes;
+    L.y_bytes = align_up((int64_t)T * topk * H * 4, 256);
+    L.total = L.y_off + L.y_bytes;
+    return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_last_error(void) { return g_err; }
+
+int64_t moe_align_sort_capacity(int T, int topk, int E, int block_m) {
+    if (T < 0 || topk < 1 || E < 1 || !valid_bm(block_m)) return -1;
+    return capacity(T, topk, E, block_m);
+}
+
+int moe_default_block_m(int T, int topk, int E) {
+    (void)topk;
+    (void)E;
+    if (T <= 16) return 16;
+    if (T <= 32) return 32;
+    return 64;
+}
+
+moe_status moe_route_topk(const float* logits, int T, int E, int topk, int renormalize,
+                          int32_t* topk_ids, float* topk_weights, void* stream) {
+    if (T < 0) return fail(MOE_ERR_INVALID_ARG, "moe_route_topk: T=%d < 0", T);
+    if (E < 1 || E > 1024) return fail(MOE_ERR_UNSUPPORTED, "moe_route_topk: E=%d outside [1, 1024]", E);
+    if (topk < 1 || topk > E) return fail(MOE_ERR_INVALID_ARG, "moe_route_topk: topk=%d outside [1, E=%d]", topk, E);
+    if (topk > 64) return fail(MOE_ERR_UNSUPPORTED, "moe_route_topk: topk=%d > 64", topk);
+    if (T == 0) return MOE_OK;
+    if (!logits || !topk_ids || !topk_weights)
+        return fail(MOE_ERR_INVALID_ARG, "moe_route_topk: null pointer");
+    if (!aligned(logits, 4) || !aligned(topk_ids, 4) || !aligned(topk_weights, 4))
+        return fail(MOE_ERR_INVALID_ARG, "moe_route_topk: misaligned pointer");
+    return hip_status(moe::launch_route_topk(logits, T, E, topk, renormalize, topk_ids, topk_weights,
+                                             (hipStream_t)stream),
+                      "moe_route_topk");
+}
+
+moe_status moe_align_sort(const int32_t* topk_ids, int T, int topk, int E, int block_m,
+                          int32_t* sorted_ids, int32_t* block_expert, int32_t* expert_offsets,
+                          int32_t* num_post_pad, void* stream) {
+    if (T < 0 || topk < 1) return fail(MOE_ERR_INVALID_ARG, "moe_align_sort: T=%d topk=%d", T, topk);
+    if (E < 1 || E > 1024) return fail(MOE_ERR_UNSUPPORTED, "moe_align_sort: E=%d outside [1, 1024]", E);
+    if (!valid_bm(block_m))
+        return fail(MOE_ERR_INVALID_ARG, "moe_align_sort: block_m=%d not in {16,32,64,128,256}", block_m);
+    const int64_t P = (int64_t)T * topk;
+    const int64_t cap = capacity(T, topk, E, block_m);
+    if (P + cap >= (int64_t)0x7fffffff)
+        return fail(MOE_ERR_UNSUPPORTED, "moe_align_sort: T*topk=%lld too large", (long long)P);
+    if (!expert_offsets || !num_post_pad || (P > 0 && (!topk_ids || !sorted_ids || !block_expert)))
+        return fail(MOE_ERR_INVALID_ARG, "moe_align_sort: null pointer");
+    if (!aligned(topk_ids, 4) || !aligned(sorted_ids, 4) || !aligned(block_expert, 4) ||
+        !aligned(expert_offsets, 4) || !aligned(num_post_pad, 4))
+        return fail(MOE_ERR_INVALID_ARG, "moe_align_sort: misaligned pointer");
+    return hip_status(moe::launch_align_sort(topk_ids, (int)P, E, block_m, cap, sorted_ids, block_expert,
+                                             expert_offsets, num_post_pad, (hipStream_t)stream),
+                      "moe_align_sort");
+}
+
+int64_t moe_a16w4_workspace_size(int T, int H, int I, int E, int topk, int block_m) {
+    if (T < 0 || H < 32 || I < 32 || E < 1 || topk < 1 || !valid_bm(block_m)) return -1;
+    return ws_layout(T, H, I, E, topk, block_m).total;
+}
+
+moe_status moe_a16w4_forward(const uint16_t* x, const uint8_t* w13, const void* w13_scale,
+                             const uint8_t* w2, const void* w2_scale, moe_wfmt fmt, moe_act act,
+                             const int32_t* topk_ids, const float* topk_weights,
+                             const int32_t* sorted_ids, const int32_t* block_expert,
+                             const int32_t* num_post_pad, int T, int H, int I, int E, int topk,
+                             int block_m, uint16_t* out, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+    return moe_a16w4_forward_stages(x, w13, w13_scale, w2, w2_scale, fmt, act, topk_ids,
+                                    topk_weights, sorted_ids, block_expert, num_post_pad, T, H, I,
+                                    E, topk, block_m, out, workspace, workspace_bytes,
+                                    MOE_STAGE_ALL, stream);
+}
+
+moe_status moe_a16w4_forward_stages(const uint16_t* x, const uint8_t* w13, const void* w13_scale,
+                                    const uint8_t* w2, const void* w2_scale, moe_wfmt fmt,
+                                    moe_act act, const int32_t* topk_ids,
+                                    const float* topk_weights, const int32_t* sorted_ids,
+                                    const int32_t* block_expert, const int32_t* num_post_pad, int T,
+                                    int H, int I, int E, int topk, int block_m, uint16_t* out,
+                                    void* workspace, size_t workspace_bytes, unsigned stages,
+                                    void* stream) {
+    const char* fn = "moe_a16w4_forward";
+    if (stages == 0 || (stages & ~MOE_STAGE_ALL))
+        return fail(MOE_ERR_INVALID_ARG, "%s: stage mask 0x%x invalid", fn, stages);
+    if (act != MOE_ACT_SWIGLU)
+        return fail(MOE_ERR_UNSUPPORTED, "%s: activation %d is not implemented (only SwiGLU); "
+                    "refusing to compute a different activation", fn, (int)act);
+    if (fmt != MOE_W_MXFP4 && fmt != MOE_W_INT4G32)
+        return fail(MOE_ERR_UNSUPPORTED, "%s: weight format %d unknown", fn, (int)fmt);
+    if (T < 0) return fail(MOE_ERR_INVALID_ARG, "%s: T=%d < 0", fn, T);
+    if (H < 32 || H % 32 != 0) return fail(MOE_ERR_INVALID_ARG, "%s: H=%d must be a positive multiple of 32", fn, H);
+    if (I < 32 || I % 32 != 0) return fail(MOE_ERR_INVALID_ARG, "%s: I=%d must be a positive multiple of 32", fn, I);
+    if (E < 1) return fail(MOE_ERR_INVALID_ARG, "%s: E=%d < 1", fn, E);
+    if (topk < 1 || topk > E) return fail(MOE_ERR_INVALID_ARG, "%s: topk=%d outside [1, E=%d]", fn, topk, E);
+    if (!valid_bm(block_m)) return fail(MOE_ERR_INVALID_ARG, "%s: block_m=%d invalid", fn, block_m);
+    if (!forward_bm(block_m))
+        return fail(MOE_ERR_UNSUPPORTED, "%s: block_m=%d not implemented (16, 32, 64)", fn, block_m);
+    const int64_t P = (int64_t)T * topk;
+    const int64_t cap = capacity(T, topk, E, block_m);
+    if (P + cap >= (int64_t)0x7fffffff || (int64_t)T * H >= ((int64_t)1 << 40))
+        return fail(MOE_ERR_UNSUPPORTED, "%s: problem too large", fn);
+    if (T == 0) return MOE_OK;
+    const void* ptrs[] = {x, w13, w13_scale, w2, w2_scale, topk_ids, topk_weights,
+                          sorted_ids, block_expert, num_post_pad, out, workspace};
+    for (const void* p : ptrs)
+        if (!p) return fail(MOE_ERR_INVALID_ARG, "%s: null pointer", fn);
+    for (const void* p : ptrs)
+        if (!aligned(p, 16)) return fail(MOE_ERR_INVALID_ARG, "%s: pointer %p not 16-byte aligned", fn, p);
+    if (!aligned(workspace, 256)) return fail(MOE_ERR_INVALID_ARG, "%s: workspace not 256-byte aligned", fn);
+    const WsLayout L = ws_layout(T, H, I, E, topk, block_m);
+    if ((int64_t)workspace_bytes < L.total)
+        return fail(MOE_ERR_INVALID_ARG, "%s: workspace %zu bytes < %lld needed", fn, workspace_bytes,
+                    (long long)L.total);
+
+    moe::MoeGemmArgs a;
+    a.x = x;
+    a.w13 = w13;
+    a.w13_scale = w13_scale;
+    a.w2 = w2;
+    a.w2_scale = w2_scale;
+    a.sorted_ids = sorted_ids;
+    a.block_expert = block_expert;
+    a.num_post_pad = num_post_pad;
+    a.h = (uint16_t*)((char*)workspace + L.h_off);
+    a.y = (float*)((char*)workspace + L.y_off);
+    a.T = T;
+    a.H = H;
+    a.I = I;
+    a.E = E;
+    a.topk = topk;
+    a.bm = block_m;
+    a.cap = cap;
+    a.fmt = (int)fmt;
+    hipStream_t s = (hipStream_t)stream;
+    moe_status st = MOE_OK;
+    if (stages & MOE_STAGE_GATE_UP) {
+        st = hip_status(moe::launch_stage1(a, s), "moe_a16w4_forward (gate_up)");
+        if (st != MOE_OK) return st;
+    }
+    if (stages & MOE_STAGE_DOWN) {
+        st = hip_status(moe::launch_stage2(a, s), "moe_a16w4_forward (down)");
+        if (st != MOE_OK) return st;
+    }
+    if (stages & MOE_STAGE_COMBINE)
+        st = hip_status(moe::launch_combine(a.y, topk_ids, topk_weights, T, H, E, topk, out, s),
+                        "moe_a16w4_forward (combine)");
+    return st;
+}
+
+moe_status mxfp4_to_int4g32_requant(const uint8_t* w, const uint8_t* scale_e8m0, int E, int N, int K,
+                                    int expert_lo, int expert_hi, uint8_t* w_int4,
+                                    uint16_t* scale_bf16, void* stream) {
+    const char* fn = "mxfp4_to_int4g32_requant";
+    if (E < 1 || N < 1) return fail(MOE_ERR_INVALID_ARG, "%s: E=%d N=%d", fn, E, N);
+    if (K < 32 || K % 32 != 0) return fail(MOE_ERR_INVALID_ARG, "%s: K=%d must be a positive multiple of 32", fn, K);
+    if (expert_lo < 0 || expert_lo > expert_hi || expert_hi > E)
+        return fail(MOE_ERR_INVALID_ARG, "%s: expert range [%d, %d) outside [0, %d]", fn, expert_lo, expert_hi, E);
+    if (expert_lo == expert_hi) return MOE_OK;
+    if (!w || !scale_e8m0 || !w_int4 || !scale_bf16) return fail(MOE_ERR_INVALID_ARG, "%s: null pointer", fn);
+    if (!aligned(w, 16) || !aligned(w_int4, 16) || !aligned(scale_bf16, 2))
+        return fail(MOE_ERR_INVALID_ARG, "%s: misaligned pointer", fn);
+    return hip_status(moe::launch_requant(w, scale_e8m0, N, K, expert_lo, expert_hi, w_int4, scale_bf16,
+                                          (hipStream_t)stream),
+                      fn);
+}
+
+}  // extern "C"

@@ -1,0 +1,113 @@
+// Token-to-expert align/sort: group the (token, slot) pairs by expert, in
+// ascending pair index within each expert, and pad every expert segment to
+// a multiple of the GEMM block. The two-stage MoE GEMM of the pages (the
+// MXFP4-to-int4 pull request, Test plan) consumes such per-expert blocks;
+// the grouping rule itself is the plain stable one.
+//
+// One 1024-thread workgroup. Counts come from LDS atomic adds (order does
+// not matter for a count). Positions never come from atomic order: pairs
+// are processed in tiles of 1024, each wave ORs one bit per pair into a
+// per-(wave, expert) 64-bit mask, and a pair's rank is the popcount of the
+// bits below it plus the counts of earlier waves and tiles -- a stable
+// counting sort, bit-identical run to run.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace moe {
+
+constexpr int kSortThreads = 1024;
+constexpr int kSortWaves = kSortThreads / 64;
+constexpr int kMaxExperts = 1024;
+
+__global__ __launch_bounds__(kSortThreads) void align_sort_kernel(
+    const int32_t* __restrict__ ids, int P, int E, int bm, int64_t cap,
+    int32_t* __restrict__ sorted_ids, int32_t* __restrict__ block_expert,
+    int32_t* __restrict__ expert_offsets, int32_t* __restrict__ num_post_pad) {
+    __shared__ unsigned long long masks[kSortWaves * kMaxExperts];
+    __shared__ int counts[kMaxExperts];
+    __shared__ int running[kMaxExperts];
+    __shared__ int offs[kMaxExperts + 1];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wv = tid >> 6;
+
+    for (int e = tid; e < E; e += kSortThreads) {
+        counts[e] = 0;
+        running[e] = 0;
+    }
+    __syncthreads();
+    for (int p = tid; p < P; p += kSortThreads) {
+        const int e = ids[p];
+        if ((unsigned)e < (unsigned)E) atomicAdd(&counts[e], 1);
+    }
+    __syncthreads();
+
+    // Exclusive scan of the padded segment lengths (wave 0, 64 at a time).
+    if (wv == 0) {
+        int carry = 0;
+        for (int base = 0; base < E; base += 64) {
+            const int e = base + lane;
+            const int c = e < E ? counts[e] : 0;
+            const int padded = (c + bm - 1) / bm * bm;
+            int incl = padded;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const int o = __shfl_up(incl, off);
+                if (lane >= off) incl += o;
+            }
+            if (e < E) offs[e] = carry + incl - padded;
+            carry += __shfl(incl, 63);
+        }
+        if (lane == 0) offs[E] = carry;
+    }
+    __syncthreads();
+
+    const int total = offs[E];
+    for (int e = tid; e <= E; e += kSortThreads) expert_offsets[e] = offs[e];
+    if (tid == 0) num_post_pad[0] = total;
+
+    // Padding rows of every segment, block -> expert map, and the unused tail.
+    // These rows are disjoint from the rows the scatter below writes.
+    for (int e = wv; e < E; e += kSortWaves) {
+        const int start = offs[e], end = offs[e + 1], c = counts[e];
+        for (int r = start + c + lane; r < end; r += 64) sorted_ids[r] = P;
+        for (int b = start / bm + lane; b < end / bm; b += 64) block_expert[b] = e;
+    }
+    for (int64_t r = total + tid; r < cap; r += kSortThreads) sorted_ids[r] = P;
+    for (int64_t b = total / bm + tid; b < cap / bm; b += kSortThreads) block_expert[b] = -1;
+
+    // Stable scatter, 1024 pairs per tile.
+    for (int base = 0; base < P; base += kSortThreads) {
+        for (int i = tid; i < kSortWaves * E; i += kSortThreads) masks[i] = 0ull;
+        __syncthreads();
+        const int p = base + tid;
+        const int e = p < P ? ids[p] : -1;
+        const bool valid = (unsigned)e < (unsigned)E;
+        if (valid) atomicOr(&masks[wv * E + e], 1ull << lane);
+        __syncthreads();
+        if (valid) {
+            int rank = running[e];
+            for (int v = 0; v < wv; ++v) rank += __popcll(masks[v * E + e]);
+            rank += __popcll(masks[wv * E + e] & ((1ull << lane) - 1ull));
+            sorted_ids[offs[e] + rank] = p;
+        }
+        __syncthreads();
+        for (int ee = tid; ee < E; ee += kSortThreads) {
+            int s = 0;
+            for (int v = 0; v < kSortWaves; ++v) s += __popcll(masks[v * E + ee]);
+            running[ee] += s;
+        }
+        __syncthreads();
+    }
+}
+
+hipError_t launch_align_sort(const int32_t* ids, int P, int E, int bm, int64_t cap,
+                             int32_t* sorted_ids, int32_t* block_expert, int32_t* expert_offsets,
+                             int32_t* num_post_pad, hipStream_t s) {
+    hipLaunchKernelGGL(align_sort_kernel, dim3(1), dim3(kSortThreads), 0, s, ids, P, E, bm, cap,
+                       sorted_ids, block_expert, expert_offsets, num_post_pad);
+    return hipGetLastError();
+}
+
+}  // namespace moe

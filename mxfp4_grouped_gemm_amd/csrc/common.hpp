@@ -1,0 +1,89 @@
+// Shared device-side types and helpers for the gfx950 (CDNA4) kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+// Weight formats (values match moe_wfmt).
+constexpr int kFmtMxfp4 = 0;
+constexpr int kFmtInt4g32 = 1;
+
+// The e8m0 block scale 2^(s-127) as the float operand of the gfx950 scaled
+// fp4 converts. Those instructions use only the exponent of that operand,
+// so the scale is applied exactly; s == 0 needs the subnormal 2^-127.
+__device__ __forceinline__ float e8m0_scale_operand(uint32_t s) {
+    return __uint_as_float(s ? (s << 23) : 0x00400000u);
+}
+
+// Eight e2m1 values packed in one dword (element 2b in the low nibble of
+// byte b) -> eight bf16 in k order, each multiplied by the block scale.
+// v_cvt_scalef32_pk_bf16_fp4 converts one byte (low nibble first).
+__device__ __forceinline__ bf16x8 mxfp4x8_to_bf16(uint32_t d, float scale) {
+    bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, scale, 0);
+    bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, scale, 1);
+    bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, scale, 2);
+    bf16x2 e = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(d, scale, 3);
+    bf16x4 ab = __builtin_shufflevector(a, b, 0, 1, 2, 3);
+    bf16x4 ce = __builtin_shufflevector(c, e, 0, 1, 2, 3);
+    return __builtin_shufflevector(ab, ce, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Eight two's-complement int4 codes packed in one dword -> eight bf16
+// holding (code + 136), i.e. 128 + (code ^ 8), exactly. The nibble lands in
+// the low mantissa bits of 128.0 (bf16 0x4300, ulp 1). Output element
+// order: nibbles {0, 4, 1, 5, 2, 6, 3, 7} -- the activation operand must use
+// the same permutation (see perm_x_int4).
+__device__ __forceinline__ bf16x8 int4x8_to_bf16_biased(uint32_t d) {
+    const uint32_t u = d ^ 0x88888888u;
+    u32x4 r;
+    r[0] = (u & 0x000F000Fu) | 0x43004300u;
+    r[1] = ((u >> 4) & 0x000F000Fu) | 0x43004300u;
+    r[2] = ((u >> 8) & 0x000F000Fu) | 0x43004300u;
+    r[3] = ((u >> 12) & 0x000F000Fu) | 0x43004300u;
+    return __builtin_bit_cast(bf16x8, r);
+}
+
+// Reorder eight bf16 activations (k order 0..7) into the nibble order that
+// int4x8_to_bf16_biased produces: {0, 4, 1, 5, 2, 6, 3, 7}.
+__device__ __forceinline__ bf16x8 perm_x_int4(bf16x8 v) {
+    return __builtin_shufflevector(v, v, 0, 4, 1, 5, 2, 6, 3, 7);
+}
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// float -> bf16 bits, round to nearest even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+    __bf16 h = (__bf16)f;
+    return __builtin_bit_cast(uint16_t, h);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    bf16x2 v;
+    v[0] = (__bf16)lo;
+    v[1] = (__bf16)hi;
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// silu(g) * u in fp32. For very negative g, expf(-g) overflows to +inf and
+// the quotient is -0 (never NaN).
+__device__ __forceinline__ float swiglu(float g, float u) {
+    return g / (1.0f + expf(-g)) * u;
+}
+
+}  // namespace moe

@@ -1,0 +1,44 @@
+// Host-side launchers of the kernels; each checks nothing (the C ABI in
+// abi.cpp validates first) and returns the launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+hipError_t launch_route_topk(const float* logits, int T, int E, int topk, int renorm, int32_t* ids,
+                             float* weights, hipStream_t s);
+
+hipError_t launch_align_sort(const int32_t* ids, int P, int E, int bm, int64_t cap,
+                             int32_t* sorted_ids, int32_t* block_expert, int32_t* expert_offsets,
+                             int32_t* num_post_pad, hipStream_t s);
+
+// Problem description shared by the two GEMM stages.
+struct MoeGemmArgs {
+    const uint16_t* x;       // bf16 [T, H]
+    const uint8_t* w13;      // [E, 2I, H/2]
+    const void* w13_scale;   // [E, 2I, H/32]
+    const uint8_t* w2;       // [E, H, I/2]
+    const void* w2_scale;    // [E, H, I/32]
+    const int32_t* sorted_ids;
+    const int32_t* block_expert;
+    const int32_t* num_post_pad;
+    uint16_t* h;             // bf16 [cap, I]   (workspace)
+    float* y;                // fp32 [P, H]     (workspace)
+    int T, H, I, E, topk, bm;
+    int64_t cap;
+    int fmt;
+};
+
+hipError_t launch_stage1(const MoeGemmArgs& a, hipStream_t s);
+hipError_t launch_stage2(const MoeGemmArgs& a, hipStream_t s);
+
+hipError_t launch_combine(const float* y, const int32_t* ids, const float* weights, int T, int H,
+                          int E, int topk, uint16_t* out, hipStream_t s);
+
+hipError_t launch_requant(const uint8_t* w, const uint8_t* scale, int N, int K, int lo, int hi,
+                          uint8_t* q, uint16_t* qs, hipStream_t s);
+
+}  // namespace moe

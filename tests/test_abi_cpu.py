@@ -1,0 +1,114 @@
+"""Host-side checks of the C ABI (no GPU needed; nothing is launched).
+
+* the library loads and exports every function include/moe_a16w4.h declares;
+* host logic: capacity, workspace size, default block size;
+* fail-closed validation: bad shapes, ranges, activations and formats return
+  an error status before any launch (null device pointers prove that no
+  kernel was enqueued -- the calls would fault otherwise).
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_a16w4.h")
+
+
+@pytest.fixture(scope="module")
+def moe():
+    from mxfp4_grouped_gemm_amd import build as b
+    if not os.path.exists(b.LIB):
+        b.build()
+    import mxfp4_grouped_gemm_amd as m
+    return m
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s+(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_expected_entry_points():
+    fns = header_functions()
+    for name in ("moe_route_topk", "moe_align_sort", "moe_a16w4_forward", "mxfp4_to_int4g32_requant",
+                 "moe_align_sort_capacity", "moe_a16w4_workspace_size", "moe_last_error",
+                 "moe_default_block_m"):
+        assert name in fns, name
+
+
+def test_library_exports_every_declared_symbol(moe):
+    fns = header_functions()
+    out = subprocess.run(["nm", "-D", "--defined-only", moe.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for name in fns:
+        assert name in exported, f"{name} declared in the header but not exported"
+        assert hasattr(moe.lib, name)
+    assert sorted(moe.EXPORTS) == fns
+
+
+def test_capacity_matches_definition(moe):
+    import oracle
+    for T, k, E, bm in [(1, 15, 112, 16), (32, 15, 112, 32), (1024, 15, 112, 64), (4, 2, 8, 16),
+                        (0, 2, 8, 16), (3, 8, 8, 256), (7, 1, 1, 128)]:
+        assert moe.moe_align_sort_capacity(T, k, E, bm) == oracle.align_capacity(T, k, E, bm)
+    assert moe.moe_align_sort_capacity(1, 1, 1, 48) == -1
+    assert moe.moe_align_sort_capacity(-1, 1, 1, 16) == -1
+
+
+def test_workspace_and_block_m(moe):
+    assert moe.moe_a16w4_workspace_size(1, 3584, 3072, 112, 15, 16) > 0
+    assert moe.moe_a16w4_workspace_size(1, 16, 3072, 112, 15, 16) == -1
+    a = moe.moe_a16w4_workspace_size(4, 256, 128, 8, 2, 16)
+    b = moe.moe_a16w4_workspace_size(8, 256, 128, 8, 2, 16)
+    assert 0 < a <= b and a % 256 == 0
+    for T in (1, 4, 16, 32, 64, 1024):
+        assert moe.moe_default_block_m(T, 15, 112) in (16, 32, 64, 128)
+
+
+def _fwd(moe, act=0, fmt=0, T=4, H=256, I=128, E=8, topk=2, bm=16, ws=1 << 20):
+    n = None
+    return moe.lib.moe_a16w4_forward(n, n, n, n, n, fmt, act, n, n, n, n, n, T, H, I, E, topk, bm,
+                                     n, n, ws, n)
+
+
+def test_forward_fails_closed(moe):
+    st = _fwd(moe, act=1)
+    assert st == moe.MOE_ERR_UNSUPPORTED and "activation" in moe.moe_last_error()
+    assert _fwd(moe, fmt=5) == moe.MOE_ERR_UNSUPPORTED
+    assert _fwd(moe, H=48) == moe.MOE_ERR_INVALID_ARG
+    assert _fwd(moe, I=100) == moe.MOE_ERR_INVALID_ARG
+    assert _fwd(moe, topk=9) == moe.MOE_ERR_INVALID_ARG
+    assert _fwd(moe, bm=48) == moe.MOE_ERR_INVALID_ARG
+    assert _fwd(moe, T=-1) == moe.MOE_ERR_INVALID_ARG
+    assert _fwd(moe) == moe.MOE_ERR_INVALID_ARG  # null pointers
+    assert "null" in moe.moe_last_error()
+    assert _fwd(moe, T=0) == moe.MOE_OK  # T == 0: nothing to do
+
+
+def test_route_sort_requant_validation(moe):
+    L, n = moe.lib, None
+    assert L.moe_route_topk(n, 1, 0, 1, 1, n, n, n) == moe.MOE_ERR_UNSUPPORTED
+    assert L.moe_route_topk(n, 1, 2000, 1, 1, n, n, n) == moe.MOE_ERR_UNSUPPORTED
+    assert L.moe_route_topk(n, 1, 8, 9, 1, n, n, n) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_route_topk(n, 1, 128, 65, 1, n, n, n) == moe.MOE_ERR_UNSUPPORTED
+    assert L.moe_route_topk(n, 0, 8, 2, 1, n, n, n) == moe.MOE_OK
+    assert L.moe_route_topk(n, 2, 8, 2, 1, n, n, n) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_align_sort(n, 4, 2, 8, 24, n, n, n, n, n) == moe.MOE_ERR_INVALID_ARG
+    assert L.moe_align_sort(n, 4, 2, 4096, 16, n, n, n, n, n) == moe.MOE_ERR_UNSUPPORTED
+    assert L.moe_align_sort(n, 4, 2, 8, 16, n, n, n, n, n) == moe.MOE_ERR_INVALID_ARG
+    assert L.mxfp4_to_int4g32_requant(n, n, 8, 16, 64, 3, 2, n, n, n) == moe.MOE_ERR_INVALID_ARG
+    assert L.mxfp4_to_int4g32_requant(n, n, 8, 16, 64, 0, 9, n, n, n) == moe.MOE_ERR_INVALID_ARG
+    assert L.mxfp4_to_int4g32_requant(n, n, 8, 16, 40, 0, 8, n, n, n) == moe.MOE_ERR_INVALID_ARG
+    assert L.mxfp4_to_int4g32_requant(n, n, 8, 16, 64, 4, 4, n, n, n) == moe.MOE_OK
+    assert L.mxfp4_to_int4g32_requant(n, n, 8, 16, 64, 0, 8, n, n, n) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_python_binding_rejects_host_tensors(moe):
+    import torch
+    with pytest.raises(ValueError):
+        moe.moe_route_topk(torch.zeros(2, 8), 2)

@@ -1,0 +1,421 @@
+"""GPU parity of the HIP path against the CPU oracle (MI355X / gfx950).
+
+Bars (fixed here):
+  * routing ids, align/sort outputs, requantized int4 codes and bf16 scales:
+    bit-exact;
+  * routing weights: |gpu - oracle| <= 1e-5 * weight + 1e-7 (fp32 exp vs the
+    oracle's float64);
+  * MoE outputs: max |gpu - oracle| <= 2e-2 * RMS(oracle output) over the
+    compared rows.
+Full-size workloads (H=3584, I=3072, E=112, topk=15) run the whole layer on
+the GPU in the benchmark's launch configuration and compare sampled tokens,
+which the oracle computes one by one.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2
+
+
+@pytest.fixture(scope="module")
+def moe():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import mxfp4_grouped_gemm_amd as m
+    return m
+
+
+def dev(a, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.view(dtype)
+    return t.cuda()
+
+
+def x_dev(wl):
+    return dev(wl.x.view(np.int16), torch.bfloat16)
+
+
+def weights_dev(wl):
+    return dev(wl.w13), dev(wl.w13_scale), dev(wl.w2), dev(wl.w2_scale)
+
+
+def bf16_host(t):
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def out_f64(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def check_close(got, ref, what):
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    err = float(np.max(np.abs(got - ref))) if ref.size else 0.0
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    assert err <= TOL * rms, f"{what}: max|err| {err:.4g} > {TOL} * RMS {rms:.4g}"
+    return err, rms
+
+
+def check_close_bf16_out(got, ref, what):
+    """Edge-case shapes: the bar above plus the rounding of the exact result to
+    the layer's bf16 output, which alone can exceed 2e-2 * RMS when a few
+    outputs are many RMS large (small K, heavy-tailed SwiGLU products):
+    |gpu_i - ref_i| <= 2e-2 * RMS + 2^-8 * |ref_i| (half a bf16 ulp of
+    ref_i is at most 2^-8 * |ref_i|)."""
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    assert np.all(np.isfinite(got)), f"{what}: non-finite output"
+    excess = np.abs(got - ref) - 2.0 ** -8 * np.abs(ref)
+    worst = float(np.max(excess)) if ref.size else 0.0
+    assert worst <= TOL * rms, f"{what}: max(|err| - 2^-8|ref|) {worst:.4g} > {TOL} * RMS {rms:.4g}"
+
+
+def run_layer(moe, wl, topk, fmt=0, w=None, bm=None):
+    x = x_dev(wl)
+    logits = dev(wl.logits)
+    w13, w13s, w2, w2s = weights_dev(wl) if w is None else w
+    out = moe.moe_a16w4_layer(x, logits, w13, w13s, w2, w2s, topk, fmt=fmt, block_m=bm)
+    torch.cuda.synchronize()
+    return out
+
+
+# ----------------------------------------------------------------- routing --
+
+ROUTE_CASES = [("tiny", None), ("decode_t1", None), ("decode_t32", None), ("skewed_t16", None),
+               ("prefill_t1024", None)]
+
+
+@pytest.mark.parametrize("name,_", ROUTE_CASES)
+def test_route_matches_oracle(moe, name, _):
+    spec = synth.specs()[name]
+    wl = synth.make(spec, with_weights=False)
+    ids, w = moe.moe_route_topk(dev(wl.logits), spec.topk)
+    torch.cuda.synchronize()
+    rids, rw = oracle.route_topk(wl.logits, spec.topk)
+    assert np.array_equal(ids.cpu().numpy(), rids)
+    got = w.cpu().numpy()
+    assert np.all(np.abs(got - rw) <= 1e-5 * rw + 1e-7)
+
+
+@pytest.mark.parametrize("T,E,topk,renorm,ties", [(5, 200, 7, True, False), (3, 1024, 64, True, False),
+                                                  (9, 64, 64, False, False), (6, 30, 5, True, True),
+                                                  (33, 1, 1, True, False), (4, 112, 15, False, False)])
+def test_route_edge_cases(moe, T, E, topk, renorm, ties):
+    rng = np.random.default_rng(T * 7 + E)
+    if ties:
+        logits = rng.integers(-2, 3, size=(T, E)).astype(np.float32)
+    else:
+        logits = rng.standard_normal((T, E)).astype(np.float32) * 3
+    ids, w = moe.moe_route_topk(dev(logits), topk, renormalize=renorm)
+    torch.cuda.synchronize()
+    rids, rw = oracle.route_topk(logits, topk, renormalize=renorm)
+    assert np.array_equal(ids.cpu().numpy(), rids)
+    assert np.all(np.abs(w.cpu().numpy() - rw) <= 1e-5 * rw + 1e-7)
+
+
+def test_route_empty(moe):
+    ids, w = moe.moe_route_topk(torch.empty((0, 8), device="cuda"), 2)
+    torch.cuda.synchronize()
+    assert ids.shape == (0, 2)
+
+
+# -------------------------------------------------------------- align/sort --
+
+def _sort_case(T, E, topk, seed, skew=False):
+    rng = np.random.default_rng(seed)
+    if skew:
+        hot = rng.choice(E, size=min(8, E), replace=False)
+        p = np.full(E, 1.0)
+        p[hot] = 40.0
+        p /= p.sum()
+        rows = [rng.choice(E, size=topk, replace=False, p=p) for _ in range(T)]
+    else:
+        rows = [rng.permutation(E)[:topk] for _ in range(T)]
+    return (np.stack(rows) if rows else np.zeros((0, topk))).astype(np.int32).reshape(T, topk)
+
+
+@pytest.mark.parametrize("T,E,topk", [(1, 112, 15), (4, 8, 2), (7, 112, 15), (32, 112, 15),
+                                      (1024, 112, 15), (100, 1000, 8), (3000, 16, 4), (0, 8, 2)])
+@pytest.mark.parametrize("bm", [16, 32, 64, 128, 256])
+def test_align_sort_bitexact(moe, T, E, topk, bm):
+    ids = _sort_case(T, E, topk, seed=T + E + bm, skew=(T == 1024))
+    s, be, off, npp = moe.moe_align_sort(dev(ids), E, bm)
+    torch.cuda.synchronize()
+    rs, rbe, roff, rnpp = oracle.align_sort(ids, E, bm)
+    cap = len(rs)
+    assert int(npp.item()) == rnpp
+    assert np.array_equal(s.cpu().numpy()[:cap], rs)
+    assert np.array_equal(be.cpu().numpy()[:cap // bm], rbe)
+    assert np.array_equal(off.cpu().numpy(), roff)
+
+
+def test_align_sort_drops_out_of_range_ids(moe):
+    ids = np.array([[0, 5], [9, 1], [-1, 3]], dtype=np.int32)
+    s, be, off, npp = moe.moe_align_sort(dev(ids), 6, 16)
+    torch.cuda.synchronize()
+    real = s.cpu().numpy()[: int(npp.item())]
+    real = real[real < ids.size]
+    assert sorted(real.tolist()) == [0, 1, 3, 5]
+
+
+def test_align_sort_deterministic(moe):
+    ids = dev(_sort_case(1024, 112, 15, seed=5, skew=True))
+    first = [t.clone() for t in moe.moe_align_sort(ids, 112, 64)]
+    for _ in range(3):
+        again = moe.moe_align_sort(ids, 112, 64)
+        for a, b in zip(first, again):
+            assert torch.equal(a, b)
+
+
+# ----------------------------------------------------------------- forward --
+
+@pytest.mark.parametrize("bm", [16, 32, 64])
+def test_forward_tiny(moe, bm):
+    wl = synth.make(synth.specs()["tiny"])
+    s = wl.spec
+    out = run_layer(moe, wl, s.topk, bm=bm)
+    ids, w = oracle.route_topk(wl.logits, s.topk)
+    ref = oracle.moe_forward(wl.x, wl.w13, wl.w13_scale, wl.w2, wl.w2_scale, 0, ids, w, I=s.I)
+    check_close(out_f64(out), ref, f"tiny bm={bm}")
+
+
+@pytest.mark.parametrize("T,H,I,E,topk,bm", [
+    (3, 96, 64, 5, 2, 16),      # ragged: K not a multiple of the 16-block step
+    (17, 256, 160, 8, 3, 16),   # rows spill into a second block
+    (33, 512, 96, 4, 4, 32),    # topk == E: every expert sees every token
+    (65, 128, 64, 6, 1, 64),    # topk == 1, several blocks per expert
+    (40, 192, 64, 1, 1, 16),    # a single expert (dense SwiGLU MLP)
+    (2, 1024, 512, 16, 16, 16),  # wide K, topk == E
+])
+def test_forward_ragged_shapes(moe, T, H, I, E, topk, bm):
+    wl = synth.small(T=T, H=H, I=I, E=E, topk=topk, seed=T + H + I)
+    out = run_layer(moe, wl, topk, bm=bm)
+    ids, w = oracle.route_topk(wl.logits, topk)
+    ref = oracle.moe_forward(wl.x, wl.w13, wl.w13_scale, wl.w2, wl.w2_scale, 0, ids, w, I=I)
+    check_close_bf16_out(out_f64(out), ref, f"T={T} H={H} I={I} E={E} k={topk} bm={bm}")
+
+
+def test_forward_precomputed_routing_matches_oracle_inputs(moe):
+    """apply()-style call: routing from the oracle fed to the GPU forward."""
+    wl = synth.small(T=9, H=256, I=128, E=8, topk=3, seed=31)
+    ids, w = oracle.route_topk(wl.logits, 3)
+    s, be, _, npp = moe.moe_align_sort(dev(ids), 8, 16)
+    w13, w13s, w2, w2s = weights_dev(wl)
+    out = moe.moe_a16w4_forward(x_dev(wl), w13, w13s, w2, w2s, dev(ids), dev(w), s, be, npp, 16)
+    torch.cuda.synchronize()
+    ref = oracle.moe_forward(wl.x, wl.w13, wl.w13_scale, wl.w2, wl.w2_scale, 0, ids, w, I=128)
+    check_close(out_f64(out), ref, "precomputed routing")
+
+
+def _sample_tokens(T, n=4, seed=0):
+    if T <= n:
+        return np.arange(T, dtype=np.int32)
+    rng = np.random.default_rng(seed)
+    mid = rng.choice(np.arange(1, T - 1), size=n - 2, replace=False)
+    return np.concatenate([[0], np.sort(mid), [T - 1]]).astype(np.int32)
+
+
+FULL = ["decode_t1", "decode_t4", "decode_t7", "decode_t16", "decode_t32", "skewed_t4", "skewed_t32",
+        "prefill_t1024"]
+
+
+@pytest.fixture(scope="module")
+def full_weights():
+    """Production-shape weights, one draw per seed, cached across tests."""
+    cache = {}
+
+    def get(name):
+        if name not in cache:
+            cache.clear()
+            torch.cuda.empty_cache()
+            wl = synth.make(synth.specs()[name])
+            cache[name] = (wl, weights_dev(wl))
+        return cache[name]
+    return get
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_forward_full_size_sampled(moe, full_weights, name):
+    wl, w = full_weights(name)
+    s = wl.spec
+    out = run_layer(moe, wl, s.topk, w=w)
+    tok = _sample_tokens(s.T, 4, seed=s.seed)
+    ids, rw = oracle.route_topk(wl.logits, s.topk)
+    ref = oracle.moe_forward(wl.x, wl.w13, wl.w13_scale, wl.w2, wl.w2_scale, 0, ids, rw, I=s.I,
+                             tokens=tok)
+    err, rms = check_close(out_f64(out)[tok], ref, name)
+    print(f"{name}: tokens {tok.tolist()} max|err| {err:.4g} RMS {rms:.4g} ({err / rms:.2e} of RMS)")
+
+
+def test_forward_deterministic(moe, full_weights):
+    wl, w = full_weights("decode_t32")
+    a = run_layer(moe, wl, 15, w=w)
+    b = run_layer(moe, wl, 15, w=w)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+# ---------------------------------------------------------------- requant --
+
+def test_requant_tiny_bitexact(moe):
+    wl = synth.make(synth.specs()["tiny"])
+    for w, s in ((wl.w13, wl.w13_scale), (wl.w2, wl.w2_scale)):
+        q, qs = moe.requantize_mxfp4_experts(dev(w), dev(s))
+        torch.cuda.synchronize()
+        rq, rs = oracle.requant_int4g32(w, s)
+        assert np.array_equal(q.cpu().numpy(), rq)
+        assert np.array_equal(bf16_host(qs), rs)
+
+
+def test_requant_edge_scales_bitexact(moe):
+    rng = np.random.default_rng(3)
+    E, N, K = 3, 8, 128
+    w = rng.integers(0, 256, size=(E, N, K // 2), dtype=np.uint8)
+    # e8m0 bytes over the whole range where every decoded value is finite in
+    # bf16 (6 * 2^(253-127) overflows); 0 gives bf16 subnormals
+    s = rng.integers(0, 253, size=(E, N, K // 32), dtype=np.uint8)
+    s[0, 0, 0] = 0
+    s[0, 0, 1] = 252
+    w[1, 1, :16] = 0x88  # an all-zero group
+    q = torch.zeros((E, N, K // 2), dtype=torch.uint8, device="cuda")
+    qs = torch.zeros((E, N, K // 32), dtype=torch.bfloat16, device="cuda")
+    moe.mxfp4_to_int4g32_requant(dev(w), dev(s), 0, E, q, qs)
+    torch.cuda.synchronize()
+    rq, rs = oracle.requant_int4g32(w, s)
+    assert np.array_equal(q.cpu().numpy(), rq)
+    assert np.array_equal(bf16_host(qs), rs)
+
+
+def test_requant_partial_range_leaves_rest(moe):
+    wl = synth.small(T=1, H=128, I=64, E=10, topk=2, seed=8)
+    w, s = dev(wl.w13), dev(wl.w13_scale)
+    q = torch.full(w.shape, 0xAA, dtype=torch.uint8, device="cuda")
+    qs = torch.full(wl.w13_scale.shape, 7.0, dtype=torch.bfloat16, device="cuda")
+    moe.mxfp4_to_int4g32_requant(w, s, 3, 6, q, qs)
+    torch.cuda.synchronize()
+    rq, rs = oracle.requant_int4g32(wl.w13, wl.w13_scale, 3, 6)
+    qn = q.cpu().numpy()
+    assert np.array_equal(qn[3:6], rq[3:6])
+    assert np.all(qn[:3] == 0xAA) and np.all(qn[6:] == 0xAA)
+    assert np.array_equal(bf16_host(qs)[3:6], rs[3:6])
+    assert torch.all(qs[:3] == 7.0) and torch.all(qs[6:] == 7.0)
+
+
+def test_int4_forward_tiny(moe):
+    wl = synth.make(synth.specs()["tiny"])
+    s = wl.spec
+    q13, s13 = moe.requantize_mxfp4_experts(dev(wl.w13), dev(wl.w13_scale))
+    q2, s2 = moe.requantize_mxfp4_experts(dev(wl.w2), dev(wl.w2_scale))
+    out = run_layer(moe, wl, s.topk, fmt=moe.MOE_W_INT4G32, w=(q13, s13, q2, s2))
+    r13, rs13 = oracle.requant_int4g32(wl.w13, wl.w13_scale)
+    r2, rs2 = oracle.requant_int4g32(wl.w2, wl.w2_scale)
+    ids, w = oracle.route_topk(wl.logits, s.topk)
+    ref = oracle.moe_forward(wl.x, r13, rs13, r2, rs2, oracle.FMT_INT4G32, ids, w, I=s.I)
+    check_close(out_f64(out), ref, "int4 tiny")
+
+
+def test_int4_full_size_t16(moe):
+    """Requantize all 112 experts eight at a time, then the int4-g32 forward at
+    T=16; the oracle requantizes the experts the sampled tokens use."""
+    spec = synth.specs()["int4_t16"]
+    wl = synth.make(spec)
+    torch.cuda.empty_cache()
+    w13, w13s, w2, w2s = weights_dev(wl)
+    q13, s13 = moe.requantize_mxfp4_experts(w13, w13s)
+    del w13, w13s
+    q2, s2 = moe.requantize_mxfp4_experts(w2, w2s)
+    del w2, w2s
+    out = run_layer(moe, wl, spec.topk, fmt=moe.MOE_W_INT4G32, w=(q13, s13, q2, s2))
+    tok = _sample_tokens(spec.T, 2, seed=4)
+    ids, rw = oracle.route_topk(wl.logits, spec.topk)
+    experts = sorted(set(ids[tok].ravel().tolist()))
+    r13 = np.zeros_like(wl.w13)
+    rs13 = np.zeros(wl.w13_scale.shape, dtype=np.uint16)
+    r2 = np.zeros_like(wl.w2)
+    rs2 = np.zeros(wl.w2_scale.shape, dtype=np.uint16)
+    for e in experts:
+        oracle.requant_int4g32(wl.w13, wl.w13_scale, e, e + 1, out=(r13, rs13))
+        oracle.requant_int4g32(wl.w2, wl.w2_scale, e, e + 1, out=(r2, rs2))
+    # the GPU codes of those experts are bit-exact too
+    e0 = experts[0]
+    assert np.array_equal(q13[e0].cpu().numpy(), r13[e0])
+    assert np.array_equal(bf16_host(s2[e0]), rs2[e0])
+    ref = oracle.moe_forward(wl.x, r13, rs13, r2, rs2, oracle.FMT_INT4G32, ids, rw, I=spec.I, tokens=tok)
+    err, rms = check_close(out_f64(out)[tok], ref, "int4 T=16")
+    print(f"int4_t16: max|err| {err:.4g} RMS {rms:.4g}")
+
+
+# ------------------------------------------------------------- error paths --
+
+def test_unsupported_activation_raises(moe):
+    wl = synth.make(synth.specs()["tiny"])
+    ids, w = oracle.route_topk(wl.logits, 2)
+    s, be, _, npp = moe.moe_align_sort(dev(ids), 8, 16)
+    w13, w13s, w2, w2s = weights_dev(wl)
+    with pytest.raises(moe.MoeError, match="activation"):
+        moe.moe_a16w4_forward(x_dev(wl), w13, w13s, w2, w2s, dev(ids), dev(w), s, be, npp, 16, act=3)
+
+
+def test_zero_tokens_is_noop(moe):
+    x = torch.empty((0, 256), dtype=torch.bfloat16, device="cuda")
+    logits = torch.empty((0, 8), dtype=torch.float32, device="cuda")
+    wl = synth.make(synth.specs()["tiny"])
+    w13, w13s, w2, w2s = weights_dev(wl)
+    out = moe.moe_a16w4_layer(x, logits, w13, w13s, w2, w2s, 2)
+    torch.cuda.synchronize()
+    assert out.shape == (0, 256)
+
+
+# ------------------------------------------------------------- graph replay --
+
+def test_graph_replay_matches_eager(moe):
+    """The whole layer captured in a HIP graph (no allocation or memset inside):
+    several replays, with eager work and host synchronisation between them,
+    each bit-identical to the eager result."""
+    wl = synth.small(T=7, H=512, I=256, E=16, topk=4, seed=77)
+    T, k, E, H, I = 7, 4, 16, 512, 256
+    x, logits = x_dev(wl), dev(wl.logits)
+    w13, w13s, w2, w2s = weights_dev(wl)
+    bm = moe.moe_default_block_m(T, k, E)
+    cap = moe.moe_align_sort_capacity(T, k, E, bm)
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    wts = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    srt = (torch.empty(cap, dtype=torch.int32, device="cuda"),
+           torch.empty(cap // bm, dtype=torch.int32, device="cuda"),
+           torch.empty(E + 1, dtype=torch.int32, device="cuda"),
+           torch.empty(1, dtype=torch.int32, device="cuda"))
+    out = torch.empty((T, H), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(moe.moe_a16w4_workspace_size(T, H, I, E, k, bm), dtype=torch.uint8, device="cuda")
+
+    def step():
+        moe.moe_route_topk(logits, k, True, ids, wts)
+        moe.moe_align_sort(ids, E, bm, out=srt)
+        moe.moe_a16w4_forward(x, w13, w13s, w2, w2s, ids, wts, srt[0], srt[1], srt[3], bm, out=out,
+                              workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    eager = out.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for r in range(4):
+        out.zero_()
+        ws.zero_()
+        srt[0].fill_(-5)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16)), f"replay {r}"
+        step()  # eager work between replays
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager.view(torch.int16))
