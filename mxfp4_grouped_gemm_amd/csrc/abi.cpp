@@ -196,12 +196,15 @@ moe_status moe_a16w4_forward_stages(const uint16_t* x, const uint8_t* w13, const
     a.fmt = (int)fmt;
     hipStream_t s = (hipStream_t)stream;
     moe_status st = MOE_OK;
+    const bool decode = block_m <= 32;
     if (stages & MOE_STAGE_GATE_UP) {
-        st = hip_status(moe::launch_stage1(a, s), "moe_a16w4_forward (gate_up)");
+        st = hip_status(decode ? moe::launch_decode_stage(a, 1, s) : moe::launch_stage1(a, s),
+                        "moe_a16w4_forward (gate_up)");
         if (st != MOE_OK) return st;
     }
     if (stages & MOE_STAGE_DOWN) {
-        st = hip_status(moe::launch_stage2(a, s), "moe_a16w4_forward (down)");
+        st = hip_status(decode ? moe::launch_decode_stage(a, 2, s) : moe::launch_stage2(a, s),
+                        "moe_a16w4_forward (down)");
         if (st != MOE_OK) return st;
     }
     if (stages & MOE_STAGE_COMBINE)

@@ -32,8 +32,11 @@ struct MoeGemmArgs {
     int fmt;
 };
 
+// Split-K workgroup kernels (any block size up to 64).
 hipError_t launch_stage1(const MoeGemmArgs& a, hipStream_t s);
 hipError_t launch_stage2(const MoeGemmArgs& a, hipStream_t s);
+// One-wave-per-tile decode kernels (block size 16 or 32); stage 1 or 2.
+hipError_t launch_decode_stage(const MoeGemmArgs& a, int stage, hipStream_t s);
 
 hipError_t launch_combine(const float* y, const int32_t* ids, const float* weights, int T, int H,
                           int E, int topk, uint16_t* out, hipStream_t s);
