@@ -107,8 +107,8 @@ class Layer:
                               device=dev)
 
     def route_sort(self):
-        self.moe.moe_route_topk(self.logits, self.k, True, self.ids, self.wts)
-        self.moe.moe_align_sort(self.ids, self.E, self.bm, out=self.sort)
+        self.moe.moe_route_align(self.logits, self.k, self.E, self.bm, True, self.ids, self.wts,
+                                 out=self.sort)
 
     def forward(self, stages=7):
         s, be, _, npp = self.sort
@@ -123,6 +123,16 @@ class Layer:
     def distinct_experts(self):
         import torch
         return int(torch.unique(self.ids).numel())
+
+
+def stage1_kernel_name(T, bm, fmt, H, I, topk):
+    """Which gate_up kernel the library launches for this shape (the rule of
+    gemv_eligible / forward_stages in the C sources, restated for the label)."""
+    rows = min(T, bm)
+    if (fmt == 0 and rows <= 4 and topk <= 16 and H <= 4096 and I <= 4096 and H % 512 == 0
+            and I % 512 == 0):
+        return "stage1_gemv_kernel"
+    return "stage1_unit_kernel" if bm <= 32 else "stage1_stream_kernel"
 
 
 def weight_bytes_per_expert(H, I, fmt):
@@ -265,7 +275,7 @@ def main():
         ach = stage1_bytes / s1_sec / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": None}
-    roof["kernel"] = "stage1_stream_kernel (grouped gate_up GEMM + SwiGLU)"
+    roof["kernel"] = stage1_kernel_name(T, layers[0].bm, fmt, H, I, k) + " (grouped gate_up GEMM + SwiGLU)"
     roof["avg_us"] = round(stage_avg[1] * 1e3, 2)
     roof["algorithmic_per_launch"] = (round(stage1_flops) if roof["bound"] == "mfma"
                                       else round(stage1_bytes))

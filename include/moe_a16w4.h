@@ -110,6 +110,16 @@ moe_status moe_align_sort(const int32_t* topk_ids, int T, int topk, int E, int b
                           int32_t* sorted_ids, int32_t* block_expert, int32_t* expert_offsets,
                           int32_t* num_post_pad, void* stream);
 
+/* moe_route_topk followed by moe_align_sort for the same arguments, with
+ * identical outputs; up to 64 tokens run as one launch that keeps the ids on
+ * chip between the two steps (the in-kernel routing of apply_monolithic on
+ * the mxfp4 API page). Limits and errors are those of the two calls; all
+ * output buffers are required (topk_ids/topk_weights [T, topk] included). */
+moe_status moe_route_align(const float* logits, int T, int E, int topk, int renormalize,
+                           int block_m, int32_t* topk_ids, float* topk_weights,
+                           int32_t* sorted_ids, int32_t* block_expert, int32_t* expert_offsets,
+                           int32_t* num_post_pad, void* stream);
+
 /* Bytes of device workspace moe_a16w4_forward needs (256-byte aligned
  * start required). Returns -1 for invalid arguments. */
 int64_t moe_a16w4_workspace_size(int T, int H, int I, int E, int topk, int block_m);
@@ -150,7 +160,10 @@ moe_status moe_a16w4_forward(const uint16_t* x, const uint8_t* w13, const void* 
  * the previous stage wrote into the same workspace for the same arguments.
  * moe_a16w4_forward == moe_a16w4_forward_stages with MOE_STAGE_ALL. Same
  * arguments, requirements and errors as moe_a16w4_forward; stages == 0 or
- * unknown bits give MOE_ERR_INVALID_ARG. */
+ * unknown bits give MOE_ERR_INVALID_ARG. For decode shapes (MXFP4, at most 4
+ * token rows per expert block, H and I multiples of 512 up to 4096,
+ * topk <= 16) the DOWN launch also performs the combine and writes out;
+ * MOE_STAGE_COMBINE then enqueues nothing. */
 #define MOE_STAGE_GATE_UP 1u
 #define MOE_STAGE_DOWN 2u
 #define MOE_STAGE_COMBINE 4u

@@ -9,7 +9,8 @@ library has not been built.
 
 Functions mirror the C ABI names:
   moe_route_topk, moe_align_sort_capacity, moe_default_block_m,
-  moe_align_sort, moe_a16w4_workspace_size, moe_a16w4_forward, moe_a16w4_forward_stages,
+  moe_align_sort, moe_route_align, moe_a16w4_workspace_size, moe_a16w4_forward,
+  moe_a16w4_forward_stages,
   mxfp4_to_int4g32_requant, moe_last_error
 plus two compositions: moe_a16w4_layer (route -> sort -> forward, the
 in-kernel routing path of apply_monolithic on the vLLM mxfp4 API page) and
@@ -33,7 +34,7 @@ MOE_STAGE_GATE_UP, MOE_STAGE_DOWN, MOE_STAGE_COMBINE, MOE_STAGE_ALL = 1, 2, 4, 7
 # Every symbol include/moe_a16w4.h declares.
 EXPORTS = (
     "moe_last_error", "moe_route_topk", "moe_align_sort_capacity", "moe_default_block_m",
-    "moe_align_sort", "moe_a16w4_workspace_size", "moe_a16w4_forward",
+    "moe_align_sort", "moe_route_align", "moe_a16w4_workspace_size", "moe_a16w4_forward",
     "moe_a16w4_forward_stages", "mxfp4_to_int4g32_requant",
 )
 
@@ -61,6 +62,8 @@ def _load():
     L.moe_default_block_m.argtypes = [i, i, i]
     L.moe_align_sort.restype = i
     L.moe_align_sort.argtypes = [p, i, i, i, i, p, p, p, p, p]
+    L.moe_route_align.restype = i
+    L.moe_route_align.argtypes = [p, i, i, i, i, i, p, p, p, p, p, p, p]
     L.moe_a16w4_workspace_size.restype = i64
     L.moe_a16w4_workspace_size.argtypes = [i, i, i, i, i, i]
     L.moe_a16w4_forward.restype = i
@@ -152,6 +155,38 @@ def moe_align_sort(topk_ids, E, block_m, out=None, stream=None):
     return sorted_ids, block_expert, offsets, npp
 
 
+def moe_route_align(logits, topk, E, block_m, renormalize=True, ids=None, weights=None, out=None,
+                    stream=None):
+    """Routing + align/sort in one call -> (ids, weights, sorted_ids, block_expert,
+    expert_offsets, num_post_pad); identical to moe_route_topk then moe_align_sort."""
+    _dev(logits, "logits", torch.float32, 2)
+    T, El = logits.shape
+    if El != E:
+        raise ValueError(f"logits have {El} experts, expected {E}")
+    dev = logits.device
+    if ids is None:
+        ids = torch.empty((T, topk), dtype=torch.int32, device=dev)
+    if weights is None:
+        weights = torch.empty((T, topk), dtype=torch.float32, device=dev)
+    _dev(ids, "ids", torch.int32)
+    _dev(weights, "weights", torch.float32)
+    cap = moe_align_sort_capacity(T, topk, E, block_m)
+    if cap < 0:
+        raise MoeError(MOE_ERR_INVALID_ARG, f"invalid sizes T={T} topk={topk} E={E} block_m={block_m}")
+    if out is None:
+        out = (torch.empty(max(cap, 1), dtype=torch.int32, device=dev),
+               torch.empty(max(cap // block_m, 1), dtype=torch.int32, device=dev),
+               torch.empty(E + 1, dtype=torch.int32, device=dev),
+               torch.empty(1, dtype=torch.int32, device=dev))
+    sorted_ids, block_expert, offsets, npp = out
+    if sorted_ids.numel() < cap or block_expert.numel() < cap // block_m or offsets.numel() < E + 1:
+        raise ValueError("align/sort output buffers too small")
+    _check(lib.moe_route_align(_ptr(logits), T, int(E), int(topk), int(bool(renormalize)),
+                               int(block_m), _ptr(ids), _ptr(weights), _ptr(sorted_ids),
+                               _ptr(block_expert), _ptr(offsets), _ptr(npp), _stream(stream)))
+    return ids, weights, sorted_ids, block_expert, offsets, npp
+
+
 def moe_a16w4_workspace_size(T, H, I, E, topk, block_m) -> int:
     return int(lib.moe_a16w4_workspace_size(int(T), int(H), int(I), int(E), int(topk), int(block_m)))
 
@@ -210,8 +245,8 @@ def moe_a16w4_layer(x, router_logits, w13, w13_scale, w2, w2_scale, topk, fmt=MO
     E = w13.shape[0]
     T = x.shape[0]
     bm = moe_default_block_m(T, topk, E) if block_m is None else block_m
-    ids, w = moe_route_topk(router_logits, topk, renormalize, stream=stream)
-    sorted_ids, block_expert, _, npp = moe_align_sort(ids, E, bm, stream=stream)
+    ids, w, sorted_ids, block_expert, _, npp = moe_route_align(router_logits, topk, E, bm, renormalize,
+                                                              stream=stream)
     return moe_a16w4_forward(x, w13, w13_scale, w2, w2_scale, ids, w, sorted_ids, block_expert, npp,
                              bm, fmt=fmt, stream=stream)
 

@@ -116,6 +116,45 @@ moe_status moe_align_sort(const int32_t* topk_ids, int T, int topk, int E, int b
                       "moe_align_sort");
 }
 
+moe_status moe_route_align(const float* logits, int T, int E, int topk, int renormalize,
+                           int block_m, int32_t* topk_ids, float* topk_weights,
+                           int32_t* sorted_ids, int32_t* block_expert, int32_t* expert_offsets,
+                           int32_t* num_post_pad, void* stream) {
+    const char* fn = "moe_route_align";
+    if (T < 0) return fail(MOE_ERR_INVALID_ARG, "%s: T=%d < 0", fn, T);
+    if (E < 1 || E > 1024) return fail(MOE_ERR_UNSUPPORTED, "%s: E=%d outside [1, 1024]", fn, E);
+    if (topk < 1 || topk > E) return fail(MOE_ERR_INVALID_ARG, "%s: topk=%d outside [1, E=%d]", fn, topk, E);
+    if (topk > 64) return fail(MOE_ERR_UNSUPPORTED, "%s: topk=%d > 64", fn, topk);
+    if (!valid_bm(block_m))
+        return fail(MOE_ERR_INVALID_ARG, "%s: block_m=%d not in {16,32,64,128,256}", fn, block_m);
+    const int64_t P = (int64_t)T * topk;
+    const int64_t cap = capacity(T, topk, E, block_m);
+    if (P + cap >= (int64_t)0x7fffffff)
+        return fail(MOE_ERR_UNSUPPORTED, "%s: T*topk=%lld too large", fn, (long long)P);
+    if (!expert_offsets || !num_post_pad ||
+        (P > 0 && (!logits || !topk_ids || !topk_weights || !sorted_ids || !block_expert)))
+        return fail(MOE_ERR_INVALID_ARG, "%s: null pointer", fn);
+    const void* ptrs[] = {logits, topk_ids, topk_weights, sorted_ids, block_expert, expert_offsets,
+                          num_post_pad};
+    for (const void* p : ptrs)
+        if (!aligned(p, 4)) return fail(MOE_ERR_INVALID_ARG, "%s: misaligned pointer", fn);
+    hipStream_t s = (hipStream_t)stream;
+    if (T > 0 && moe::route_align_fusable(T, E, topk))
+        return hip_status(moe::launch_route_align(logits, T, E, topk, renormalize, block_m, cap,
+                                                  topk_ids, topk_weights, sorted_ids, block_expert,
+                                                  expert_offsets, num_post_pad, s),
+                          fn);
+    if (T > 0) {
+        moe_status st = hip_status(moe::launch_route_topk(logits, T, E, topk, renormalize, topk_ids,
+                                                          topk_weights, s),
+                                   fn);
+        if (st != MOE_OK) return st;
+    }
+    return hip_status(moe::launch_align_sort(topk_ids, (int)P, E, block_m, cap, sorted_ids,
+                                             block_expert, expert_offsets, num_post_pad, s),
+                      fn);
+}
+
 int64_t moe_a16w4_workspace_size(int T, int H, int I, int E, int topk, int block_m) {
     if (T < 0 || H < 32 || I < 32 || E < 1 || topk < 1 || !valid_bm(block_m)) return -1;
     return ws_layout(T, H, I, E, topk, block_m).total;
@@ -194,9 +233,14 @@ moe_status moe_a16w4_forward_stages(const uint16_t* x, const uint8_t* w13, const
     a.bm = block_m;
     a.cap = cap;
     a.fmt = (int)fmt;
+    a.topk_ids = topk_ids;
+    a.topk_weights = topk_weights;
+    a.out = out;
     hipStream_t s = (hipStream_t)stream;
     moe_status st = MOE_OK;
     const bool decode = block_m <= 32;
+    // The GEMV decode path combines inside its down launch.
+    const bool combined_in_down = decode && moe::gemv_eligible(a);
     if (stages & MOE_STAGE_GATE_UP) {
         st = hip_status(decode ? moe::launch_decode_stage(a, 1, s) : moe::launch_stage1(a, s),
                         "moe_a16w4_forward (gate_up)");
@@ -207,7 +251,7 @@ moe_status moe_a16w4_forward_stages(const uint16_t* x, const uint8_t* w13, const
                         "moe_a16w4_forward (down)");
         if (st != MOE_OK) return st;
     }
-    if (stages & MOE_STAGE_COMBINE)
+    if ((stages & MOE_STAGE_COMBINE) && !combined_in_down)
         st = hip_status(moe::launch_combine(a.y, topk_ids, topk_weights, T, H, E, topk, out, s),
                         "moe_a16w4_forward (combine)");
     return st;

@@ -10,36 +10,45 @@
 // per-(wave, expert) 64-bit mask, and a pair's rank is the popcount of the
 // bits below it plus the counts of earlier waves and tiles -- a stable
 // counting sort, bit-identical run to run.
+//
+// route_align_kernel runs the routing of up to 64 tokens (route.hpp, one
+// wave per token) in the same workgroup and sorts straight from LDS, saving
+// a launch and a round trip of the ids through memory at decode sizes.
 #include "common.hpp"
 #include "launch.hpp"
+#include "route.hpp"
 
 namespace moe {
 
 constexpr int kSortThreads = 1024;
 constexpr int kSortWaves = kSortThreads / 64;
 constexpr int kMaxExperts = 1024;
+constexpr int kFusedMaxPairs = 4096;
 
-__global__ __launch_bounds__(kSortThreads) void align_sort_kernel(
-    const int32_t* __restrict__ ids, int P, int E, int bm, int64_t cap,
-    int32_t* __restrict__ sorted_ids, int32_t* __restrict__ block_expert,
-    int32_t* __restrict__ expert_offsets, int32_t* __restrict__ num_post_pad) {
-    __shared__ unsigned long long masks[kSortWaves * kMaxExperts];
-    __shared__ int counts[kMaxExperts];
-    __shared__ int running[kMaxExperts];
-    __shared__ int offs[kMaxExperts + 1];
+struct SortShared {
+    unsigned long long masks[kSortWaves * kMaxExperts];
+    int counts[kMaxExperts];
+    int running[kMaxExperts];
+    int offs[kMaxExperts + 1];
+};
 
+// ids: global or LDS (generic pointer).
+__device__ void align_sort_body(SortShared& sh, const int32_t* ids, int P, int E, int bm, int64_t cap,
+                                int32_t* __restrict__ sorted_ids, int32_t* __restrict__ block_expert,
+                                int32_t* __restrict__ expert_offsets,
+                                int32_t* __restrict__ num_post_pad) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wv = tid >> 6;
 
     for (int e = tid; e < E; e += kSortThreads) {
-        counts[e] = 0;
-        running[e] = 0;
+        sh.counts[e] = 0;
+        sh.running[e] = 0;
     }
     __syncthreads();
     for (int p = tid; p < P; p += kSortThreads) {
         const int e = ids[p];
-        if ((unsigned)e < (unsigned)E) atomicAdd(&counts[e], 1);
+        if ((unsigned)e < (unsigned)E) atomicAdd(&sh.counts[e], 1);
     }
     __syncthreads();
 
@@ -48,7 +57,7 @@ __global__ __launch_bounds__(kSortThreads) void align_sort_kernel(
         int carry = 0;
         for (int base = 0; base < E; base += 64) {
             const int e = base + lane;
-            const int c = e < E ? counts[e] : 0;
+            const int c = e < E ? sh.counts[e] : 0;
             const int padded = (c + bm - 1) / bm * bm;
             int incl = padded;
 #pragma unroll
@@ -56,21 +65,21 @@ __global__ __launch_bounds__(kSortThreads) void align_sort_kernel(
                 const int o = __shfl_up(incl, off);
                 if (lane >= off) incl += o;
             }
-            if (e < E) offs[e] = carry + incl - padded;
+            if (e < E) sh.offs[e] = carry + incl - padded;
             carry += __shfl(incl, 63);
         }
-        if (lane == 0) offs[E] = carry;
+        if (lane == 0) sh.offs[E] = carry;
     }
     __syncthreads();
 
-    const int total = offs[E];
-    for (int e = tid; e <= E; e += kSortThreads) expert_offsets[e] = offs[e];
+    const int total = sh.offs[E];
+    for (int e = tid; e <= E; e += kSortThreads) expert_offsets[e] = sh.offs[e];
     if (tid == 0) num_post_pad[0] = total;
 
     // Padding rows of every segment, block -> expert map, and the unused tail.
     // These rows are disjoint from the rows the scatter below writes.
     for (int e = wv; e < E; e += kSortWaves) {
-        const int start = offs[e], end = offs[e + 1], c = counts[e];
+        const int start = sh.offs[e], end = sh.offs[e + 1], c = sh.counts[e];
         for (int r = start + c + lane; r < end; r += 64) sorted_ids[r] = P;
         for (int b = start / bm + lane; b < end / bm; b += 64) block_expert[b] = e;
     }
@@ -79,27 +88,52 @@ __global__ __launch_bounds__(kSortThreads) void align_sort_kernel(
 
     // Stable scatter, 1024 pairs per tile.
     for (int base = 0; base < P; base += kSortThreads) {
-        for (int i = tid; i < kSortWaves * E; i += kSortThreads) masks[i] = 0ull;
+        for (int i = tid; i < kSortWaves * E; i += kSortThreads) sh.masks[i] = 0ull;
         __syncthreads();
         const int p = base + tid;
         const int e = p < P ? ids[p] : -1;
         const bool valid = (unsigned)e < (unsigned)E;
-        if (valid) atomicOr(&masks[wv * E + e], 1ull << lane);
+        if (valid) atomicOr(&sh.masks[wv * E + e], 1ull << lane);
         __syncthreads();
         if (valid) {
-            int rank = running[e];
-            for (int v = 0; v < wv; ++v) rank += __popcll(masks[v * E + e]);
-            rank += __popcll(masks[wv * E + e] & ((1ull << lane) - 1ull));
-            sorted_ids[offs[e] + rank] = p;
+            int rank = sh.running[e];
+            for (int v = 0; v < wv; ++v) rank += __popcll(sh.masks[v * E + e]);
+            rank += __popcll(sh.masks[wv * E + e] & ((1ull << lane) - 1ull));
+            sorted_ids[sh.offs[e] + rank] = p;
         }
         __syncthreads();
         for (int ee = tid; ee < E; ee += kSortThreads) {
             int s = 0;
-            for (int v = 0; v < kSortWaves; ++v) s += __popcll(masks[v * E + ee]);
-            running[ee] += s;
+            for (int v = 0; v < kSortWaves; ++v) s += __popcll(sh.masks[v * E + ee]);
+            sh.running[ee] += s;
         }
         __syncthreads();
     }
+}
+
+__global__ __launch_bounds__(kSortThreads) void align_sort_kernel(
+    const int32_t* __restrict__ ids, int P, int E, int bm, int64_t cap,
+    int32_t* __restrict__ sorted_ids, int32_t* __restrict__ block_expert,
+    int32_t* __restrict__ expert_offsets, int32_t* __restrict__ num_post_pad) {
+    __shared__ SortShared sh;
+    align_sort_body(sh, ids, P, E, bm, cap, sorted_ids, block_expert, expert_offsets, num_post_pad);
+}
+
+template <int VPL>
+__global__ __launch_bounds__(kSortThreads) void route_align_kernel(
+    const float* __restrict__ logits, int T, int E, int topk, int renorm, int bm, int64_t cap,
+    int32_t* __restrict__ ids, float* __restrict__ weights, int32_t* __restrict__ sorted_ids,
+    int32_t* __restrict__ block_expert, int32_t* __restrict__ expert_offsets,
+    int32_t* __restrict__ num_post_pad) {
+    __shared__ SortShared sh;
+    __shared__ int32_t ids_lds[kFusedMaxPairs];
+    const int wv = threadIdx.x >> 6;
+    for (int t = wv; t < T; t += kSortWaves)
+        route_token<VPL>(logits + (int64_t)t * E, E, topk, renorm, ids + (int64_t)t * topk,
+                         weights + (int64_t)t * topk, ids_lds + t * topk);
+    __syncthreads();
+    align_sort_body(sh, ids_lds, T * topk, E, bm, cap, sorted_ids, block_expert, expert_offsets,
+                    num_post_pad);
 }
 
 hipError_t launch_align_sort(const int32_t* ids, int P, int E, int bm, int64_t cap,
@@ -107,6 +141,28 @@ hipError_t launch_align_sort(const int32_t* ids, int P, int E, int bm, int64_t c
                              int32_t* num_post_pad, hipStream_t s) {
     hipLaunchKernelGGL(align_sort_kernel, dim3(1), dim3(kSortThreads), 0, s, ids, P, E, bm, cap,
                        sorted_ids, block_expert, expert_offsets, num_post_pad);
+    return hipGetLastError();
+}
+
+bool route_align_fusable(int T, int E, int topk) {
+    return T <= 64 && (int64_t)T * topk <= kFusedMaxPairs && E <= kMaxExperts;
+}
+
+hipError_t launch_route_align(const float* logits, int T, int E, int topk, int renorm, int bm,
+                              int64_t cap, int32_t* ids, float* weights, int32_t* sorted_ids,
+                              int32_t* block_expert, int32_t* expert_offsets, int32_t* num_post_pad,
+                              hipStream_t s) {
+    const dim3 grid(1), block(kSortThreads);
+    const int vpl = (E + 63) / 64;
+#define MOE_LAUNCH_RA(V)                                                                          \
+    hipLaunchKernelGGL(route_align_kernel<V>, grid, block, 0, s, logits, T, E, topk, renorm, bm, \
+                       cap, ids, weights, sorted_ids, block_expert, expert_offsets, num_post_pad)
+    if (vpl <= 1) MOE_LAUNCH_RA(1);
+    else if (vpl <= 2) MOE_LAUNCH_RA(2);
+    else if (vpl <= 4) MOE_LAUNCH_RA(4);
+    else if (vpl <= 8) MOE_LAUNCH_RA(8);
+    else MOE_LAUNCH_RA(16);
+#undef MOE_LAUNCH_RA
     return hipGetLastError();
 }
 

@@ -1,0 +1,311 @@
+// GEMV-shaped decode kernels for expert blocks of at most 4 token rows
+// (MXFP4 weights, K a multiple of 512 up to 4096).
+//
+// With one or a few activation rows per expert block, 15/16 of every MFMA
+// would idle and the MFMA operand layout (16 rows x 64 bytes per load) costs a
+// memory instruction per 64 bytes of each row. Here a wave owns 4 weight
+// rows over the whole K instead:
+//  * each load instruction reads 1 KB contiguous of one row (lane l holds MX
+//    block 64c + l of chunk c), and every load of the wave is issued up
+//    front, so a wave is one memory round trip;
+//  * the e8m0 scales of the 4 rows arrive as one 16-byte load per lane into
+//    wave-private LDS (a byte per lane per row would cost as many memory
+//    instructions as the weights);
+//  * a lane decodes its block with the scaled fp4 -> bf16 converts and
+//    accumulates v_dot2_f32_bf16 against the matching 32 activations; row
+//    sums meet with permlane32/16 swaps and DPP row rotations.
+//
+// Stage 1 is block-major (one expert block, its <= 4 rows share the weight
+// stream) and stores h by pair index. Stage 2 is token-major: a 512-thread
+// workgroup owns (token, 4 output columns), its 8 waves take the token's
+// top-k slots (expert of slot j from topk_ids), scale each slot's partial
+// sums by the router weight and meet in LDS in a fixed order, so the weighted
+// combine happens in the same launch and no per-pair output is stored.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace moe {
+
+constexpr int kGemvWaves1 = 4;  // stage 1: waves per workgroup (independent tiles)
+constexpr int kGemvWaves2 = 8;  // stage 2: waves per workgroup (slots of one token)
+constexpr int kSlotsPerWave = 2;
+
+template <int CTRL>
+__device__ __forceinline__ float ror_add(float v) {
+    return v + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+// Sum over the 16 lanes of each DPP row; every lane of the row gets the sum.
+__device__ __forceinline__ float row16_sum(float v) {
+    v = ror_add<0x128>(v);  // row_ror:8
+    v = ror_add<0x124>(v);  // row_ror:4
+    v = ror_add<0x122>(v);  // row_ror:2
+    v = ror_add<0x121>(v);  // row_ror:1
+    return v;
+}
+// v_permlane32_swap a, b exchanges lanes 32..63 of a with lanes 0..31 of b
+// (v_permlane16_swap: the odd 16-lane rows of a with the even rows of b).
+// Issued as inline asm with both registers read-write: the compiler's
+// two-result builtin lost its second result when both were used. The
+// compiler cannot see inside the asm, so the asm carries its own wait states
+// for the VALU-write -> permlane-read hazard: 3 cover the slowest producer
+// here (v_dot2c_f32_bf16; other VALU ops need 2). With 2, the last dot of
+// the lanes moved across was read stale.
+__device__ __forceinline__ void permlane32_swap(float& a, float& b) {
+    asm volatile("s_nop 2\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void permlane16_swap(float& a, float& b) {
+    asm volatile("s_nop 2\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ float swap32_add(float a, float b) {
+    permlane32_swap(a, b);
+    return a + b;
+}
+__device__ __forceinline__ float swap16_add(float a, float b) {
+    permlane16_swap(a, b);
+    return a + b;
+}
+// Reduce 4 per-lane partials over the wave: 16-lane row rho of the result
+// holds the total of v[sig(rho)], sig = (0, 2, 1, 3).
+__device__ __forceinline__ float reduce4(const float (&v)[4]) {
+    return row16_sum(swap16_add(swap32_add(v[0], v[1]), swap32_add(v[2], v[3])));
+}
+
+// Four weight rows as up to two runs of consecutive rows (run 0 -> slots
+// 0..n0-1, run 1 -> the rest).
+struct GemvRows {
+    int first0, n0, first1;
+    __device__ __forceinline__ int row(int r) const { return r < n0 ? first0 + r : first1 + (r - n0); }
+};
+
+// Loads of one wave for 4 weight rows over NCH chunks of 64 MX blocks.
+template <int NCH>
+struct GemvWeights {
+    u32x4 w[4][NCH];
+    u32x4 sc;  // this lane's 16-byte piece of the rows' scale bytes
+
+    __device__ __forceinline__ void issue(rsrc_t rw, rsrc_t rs, const GemvRows& rows, int nblk, int lane) {
+        const int p0 = rows.n0 * nblk / 16, ptot = 4 * nblk / 16;
+        uint32_t so = kOob;
+        if (lane < p0)
+            so = (uint32_t)rows.first0 * nblk + 16u * lane;
+        else if (lane < ptot)
+            so = (uint32_t)rows.first1 * nblk + 16u * (lane - p0);
+        sc = bld16(rs, so);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int c = 0; c < NCH; ++c) {
+                const int blk = 64 * c + lane;
+                w[r][c] = bld16(rw, blk < nblk ? (uint32_t)rows.row(r) * (uint32_t)(nblk * 16) + 16u * blk : kOob);
+            }
+    }
+    // Scale bytes into wave-private LDS: row slot r at [r * nblk, +nblk).
+    __device__ __forceinline__ void stage_scales(uint8_t* lds, int nblk, int lane) const {
+        if (lane < 4 * nblk / 16) *(u32x4*)(lds + 16 * lane) = sc;
+    }
+};
+
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <int NCH>
+__device__ __forceinline__ void issue_x(u32x4 (&x)[NCH][4], rsrc_t rx, uint32_t x_off, int nblk, int lane) {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        const int blk = 64 * c + lane;
+        const uint32_t o = (x_off != kOob && blk < nblk) ? x_off + 64u * blk : kOob;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) x[c][q] = bld16(rx, o + 16u * q);
+    }
+}
+
+// acc[r] += dot(weight row r, activation row) over this lane's blocks.
+template <int NCH>
+__device__ __forceinline__ void gemv_dot(const GemvWeights<NCH>& W, const uint8_t* lds_scale,
+                                         const u32x4 (&x)[NCH][4], int nblk, int lane,
+                                         float (&acc)[4]) {
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        const int blk = 64 * c + lane;
+        const int sblk = blk < nblk ? blk : nblk - 1;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float sc = e8m0_scale_operand(lds_scale[r * nblk + sblk]);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                // bf16 pairs via shufflevector: element access through a u32x4
+                // bit_cast was folded to element 0 by the compiler.
+                const bf16x8 wv = mxfp4x8_to_bf16(W.w[r][c][q], sc);
+                const bf16x8 xv = __builtin_bit_cast(bf16x8, x[c][q]);
+                acc[r] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(wv, wv, 0, 1),
+                                                         __builtin_shufflevector(xv, xv, 0, 1), acc[r], false);
+                acc[r] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(wv, wv, 2, 3),
+                                                         __builtin_shufflevector(xv, xv, 2, 3), acc[r], false);
+                acc[r] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(wv, wv, 4, 5),
+                                                         __builtin_shufflevector(xv, xv, 4, 5), acc[r], false);
+                acc[r] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(wv, wv, 6, 7),
+                                                         __builtin_shufflevector(xv, xv, 6, 7), acc[r], false);
+            }
+        }
+    }
+}
+
+// Stage 1: unit = (expert block b, columns i0, i0+1 of I): gate rows i0,
+// i0+1 and up rows I+i0, I+i0+1, against the block's <= NR token rows.
+template <int NR, int NCH>
+__global__ __launch_bounds__(kGemvWaves1 * 64) void stage1_gemv_kernel(MoeGemmArgs a) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds_scale[kGemvWaves1][4 * 64 * NCH];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar addressing
+    const int upb = a.I / 2;
+    const int64_t u = (int64_t)blockIdx.x * kGemvWaves1 + wave;
+    const int64_t b = u / upb;
+    if (b >= a.cap / a.bm) return;
+    // One round trip: the block's expert (-1 past the used blocks) and rows.
+    const int64_t row0 = b * a.bm;
+    const int e = a.block_expert[b];
+    const int P = a.T * a.topk;
+    int pair[NR], nvalid = 0;
+#pragma unroll
+    for (int m = 0; m < NR; ++m) {
+        pair[m] = a.sorted_ids[row0 + m];
+        nvalid += (pair[m] >= 0 && pair[m] < P) ? 1 : 0;
+    }
+    if (e < 0 || e >= a.E) return;
+    const int i0 = (int)(u % upb) * 2;
+    const int H = a.H, I = a.I, nblk = H / 32;
+
+    const int64_t slab_rows = 2 * (int64_t)I;
+    const rsrc_t rw = make_rsrc(a.w13 + e * slab_rows * (H / 2), (uint32_t)(slab_rows * (H / 2)));
+    const rsrc_t rs = make_rsrc((const uint8_t*)a.w13_scale + e * slab_rows * nblk, (uint32_t)(slab_rows * nblk));
+    const rsrc_t rx = make_rsrc(a.x, (uint32_t)((int64_t)a.T * H * 2));
+    // Activations first: the oldest loads, so waiting for them never waits
+    // for the weight stream issued after them.
+    u32x4 x[NR][NCH][4];
+#pragma unroll
+    for (int m = 0; m < NR; ++m)
+        issue_x<NCH>(x[m], rx, m < nvalid ? (uint32_t)(pair[m] / a.topk) * (uint32_t)(2 * H) : kOob, nblk, lane);
+    GemvWeights<NCH> W;
+    W.issue(rw, rs, GemvRows{i0, 2, I + i0}, nblk, lane);
+    W.stage_scales(lds_scale[wave], nblk, lane);
+    wave_lds_sync();
+
+#pragma unroll
+    for (int m = 0; m < NR; ++m) {
+        if (m >= nvalid) break;
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+        gemv_dot<NCH>(W, lds_scale[wave], x[m], nblk, lane, acc);
+        // acc: gate i0, gate i0+1, up i0, up i0+1. With v = (g0, u0, g1, u1)
+        // the rows after reduce4 hold (g0, g1, u0, u1); a permlane32 swap of
+        // the sum with itself puts (g0, u0) in lanes 0..15, (g1, u1) in 16..31.
+        float v[4] = {acc[0], acc[2], acc[1], acc[3]};
+        float gs = reduce4(v), us = gs;
+        permlane32_swap(gs, us);
+        if ((lane & 15) == 0 && lane < 32)
+            a.h[(int64_t)pair[m] * I + i0 + (lane >> 4)] = f32_to_bf16_bits(swiglu(gs, us));
+    }
+}
+
+// Stage 2 + combine: workgroup = (token t, output columns n0..n0+3); wave w
+// takes slots j = w + 8 s (s < kSlotsPerWave) of the token.
+template <int NCH>
+__global__ __launch_bounds__(kGemvWaves2 * 64) void stage2_gemv_tok_kernel(MoeGemmArgs a) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds_scale[kGemvWaves2][kSlotsPerWave][4 * 64 * NCH];
+    __shared__ float red[kGemvWaves2][4];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar addressing
+    const int cpt = a.H / 4;
+    const int t = (int)(blockIdx.x / cpt);
+    const int n0 = (int)(blockIdx.x % cpt) * 4;
+    const int H = a.H, I = a.I, nblk = I / 32;
+    const int topk = a.topk;
+
+    // One round trip: the slots' experts and router weights.
+    int e[kSlotsPerWave];
+    float wt[kSlotsPerWave];
+    bool ok[kSlotsPerWave];
+#pragma unroll
+    for (int s = 0; s < kSlotsPerWave; ++s) {
+        const int j = wave + kGemvWaves2 * s;
+        const int64_t p = (int64_t)t * topk + j;
+        e[s] = j < topk ? a.topk_ids[p] : -1;
+        ok[s] = (unsigned)e[s] < (unsigned)a.E;
+        wt[s] = ok[s] ? a.topk_weights[p] : 0.0f;
+    }
+    const rsrc_t rx = make_rsrc(a.h, (uint32_t)((int64_t)a.T * topk * I * 2));
+    u32x4 x[kSlotsPerWave][NCH][4];
+#pragma unroll
+    for (int s = 0; s < kSlotsPerWave; ++s) {
+        const int64_t p = (int64_t)t * topk + wave + kGemvWaves2 * s;
+        issue_x<NCH>(x[s], rx, ok[s] ? (uint32_t)p * (uint32_t)(2 * I) : kOob, nblk, lane);
+    }
+    GemvWeights<NCH> W[kSlotsPerWave];
+#pragma unroll
+    for (int s = 0; s < kSlotsPerWave; ++s) {
+        const int es = ok[s] ? e[s] : 0;
+        const rsrc_t rw = make_rsrc(a.w2 + (int64_t)es * H * (I / 2), ok[s] ? (uint32_t)((int64_t)H * (I / 2)) : 0u);
+        const rsrc_t rs = make_rsrc((const uint8_t*)a.w2_scale + (int64_t)es * H * nblk,
+                                    ok[s] ? (uint32_t)((int64_t)H * nblk) : 0u);
+        W[s].issue(rw, rs, GemvRows{n0, 4, 0}, nblk, lane);
+    }
+#pragma unroll
+    for (int s = 0; s < kSlotsPerWave; ++s) W[s].stage_scales(lds_scale[wave][s], nblk, lane);
+    wave_lds_sync();
+
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < kSlotsPerWave; ++s) {
+        if (!ok[s]) continue;  // uniform: the slot's expert is the same for the whole wave
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+        gemv_dot<NCH>(W[s], lds_scale[wave][s], x[s], nblk, lane, acc);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = fmaf(wt[s], acc[r], v[r]);
+    }
+    // Rows after reduce4: columns n0 + (0, 2, 1, 3) in 16-lane rows 0..3.
+    const float q = reduce4(v);
+    const int rho = lane >> 4;
+    if ((lane & 15) == 0) red[wave][(rho == 1) ? 2 : (rho == 2) ? 1 : rho] = q;
+    __syncthreads();
+    if (threadIdx.x < 4) {
+        float sum = 0.f;
+#pragma unroll
+        for (int w = 0; w < kGemvWaves2; ++w) sum += red[w][threadIdx.x];
+        a.out[(int64_t)t * H + n0 + threadIdx.x] = f32_to_bf16_bits(sum);
+    }
+}
+
+bool gemv_eligible(const MoeGemmArgs& a) {
+    const int max_rows = a.T < a.bm ? a.T : a.bm;
+    return a.fmt == kFmtMxfp4 && max_rows <= 4 && a.topk <= kGemvWaves2 * kSlotsPerWave &&
+           a.H <= 4096 && a.I <= 4096 && a.H % 512 == 0 && a.I % 512 == 0 &&
+           (int64_t)a.T * a.topk * a.I * 2 < 0x7fff0000LL;
+}
+
+template <int NR>
+static void launch_stage1_nr(const MoeGemmArgs& a, int nch, hipStream_t s) {
+    const int64_t units = (a.cap / a.bm) * (a.I / 2);
+    const dim3 grid((unsigned)((units + kGemvWaves1 - 1) / kGemvWaves1)), block(kGemvWaves1 * 64);
+    if (nch == 1) hipLaunchKernelGGL((stage1_gemv_kernel<NR, 1>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((stage1_gemv_kernel<NR, 2>), grid, block, 0, s, a);
+}
+
+hipError_t launch_gemv_stage(const MoeGemmArgs& a, int stage, hipStream_t s) {
+    if (stage == 1) {
+        const int nch = (a.H / 32 + 63) / 64;
+        const int rows = a.T < a.bm ? a.T : a.bm;
+        if (rows <= 1) launch_stage1_nr<1>(a, nch, s);
+        else if (rows <= 2) launch_stage1_nr<2>(a, nch, s);
+        else launch_stage1_nr<4>(a, nch, s);
+    } else {
+        const int nch = (a.I / 32 + 63) / 64;
+        const dim3 grid((unsigned)((int64_t)a.T * (a.H / 4))), block(kGemvWaves2 * 64);
+        if (nch == 1) hipLaunchKernelGGL((stage2_gemv_tok_kernel<1>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((stage2_gemv_tok_kernel<2>), grid, block, 0, s, a);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace moe

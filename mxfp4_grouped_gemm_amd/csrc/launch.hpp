@@ -15,6 +15,13 @@ hipError_t launch_align_sort(const int32_t* ids, int P, int E, int bm, int64_t c
                              int32_t* sorted_ids, int32_t* block_expert, int32_t* expert_offsets,
                              int32_t* num_post_pad, hipStream_t s);
 
+// Routing and align/sort in one workgroup (T <= 64, T*topk <= 4096).
+bool route_align_fusable(int T, int E, int topk);
+hipError_t launch_route_align(const float* logits, int T, int E, int topk, int renorm, int bm,
+                              int64_t cap, int32_t* ids, float* weights, int32_t* sorted_ids,
+                              int32_t* block_expert, int32_t* expert_offsets, int32_t* num_post_pad,
+                              hipStream_t s);
+
 // Problem description shared by the two GEMM stages.
 struct MoeGemmArgs {
     const uint16_t* x;       // bf16 [T, H]
@@ -25,8 +32,11 @@ struct MoeGemmArgs {
     const int32_t* sorted_ids;
     const int32_t* block_expert;
     const int32_t* num_post_pad;
-    uint16_t* h;             // bf16 [cap, I]   (workspace)
+    uint16_t* h;             // bf16 [cap, I]   (workspace; GEMV path: [P, I] by pair)
     float* y;                // fp32 [P, H]     (workspace)
+    const int32_t* topk_ids;     // [T, topk]
+    const float* topk_weights;   // [T, topk]
+    uint16_t* out;               // bf16 [T, H]
     int T, H, I, E, topk, bm;
     int64_t cap;
     int fmt;
@@ -37,6 +47,11 @@ hipError_t launch_stage1(const MoeGemmArgs& a, hipStream_t s);
 hipError_t launch_stage2(const MoeGemmArgs& a, hipStream_t s);
 // One-wave-per-tile decode kernels (block size 16 or 32); stage 1 or 2.
 hipError_t launch_decode_stage(const MoeGemmArgs& a, int stage, hipStream_t s);
+// GEMV-shaped decode kernels (blocks of at most 4 token rows, MXFP4, K a
+// multiple of 512 up to 4096). Their stage 2 also performs the combine and
+// writes `out`; h is stored by pair index.
+bool gemv_eligible(const MoeGemmArgs& a);
+hipError_t launch_gemv_stage(const MoeGemmArgs& a, int stage, hipStream_t s);
 
 hipError_t launch_combine(const float* y, const int32_t* ids, const float* weights, int T, int H,
                           int E, int topk, uint16_t* out, hipStream_t s);

@@ -154,6 +154,25 @@ def test_align_sort_bitexact(moe, T, E, topk, bm):
     assert np.array_equal(off.cpu().numpy(), roff)
 
 
+@pytest.mark.parametrize("name", ["tiny", "decode_t1", "decode_t7", "skewed_t32", "prefill_t1024"])
+@pytest.mark.parametrize("bm", [16, 64])
+def test_route_align_matches_oracle(moe, name, bm):
+    """The fused routing + align/sort call (one launch up to 64 tokens) gives
+    the oracle's ids, sort and offsets exactly."""
+    spec = synth.specs()[name]
+    wl = synth.make(spec, with_weights=False)
+    ids, w, s, be, off, npp = moe.moe_route_align(dev(wl.logits), spec.topk, spec.E, bm)
+    torch.cuda.synchronize()
+    rids, rw = oracle.route_topk(wl.logits, spec.topk)
+    assert np.array_equal(ids.cpu().numpy(), rids)
+    assert np.all(np.abs(w.cpu().numpy() - rw) <= 1e-5 * rw + 1e-7)
+    rs, rbe, roff, rnpp = oracle.align_sort(rids, spec.E, bm)
+    assert int(npp.item()) == rnpp
+    assert np.array_equal(s.cpu().numpy()[:len(rs)], rs)
+    assert np.array_equal(be.cpu().numpy()[:len(rs) // bm], rbe)
+    assert np.array_equal(off.cpu().numpy(), roff)
+
+
 def test_align_sort_drops_out_of_range_ids(moe):
     ids = np.array([[0, 5], [9, 1], [-1, 3]], dtype=np.int32)
     s, be, off, npp = moe.moe_align_sort(dev(ids), 6, 16)
@@ -198,6 +217,18 @@ def test_forward_ragged_shapes(moe, T, H, I, E, topk, bm):
     ids, w = oracle.route_topk(wl.logits, topk)
     ref = oracle.moe_forward(wl.x, wl.w13, wl.w13_scale, wl.w2, wl.w2_scale, 0, ids, w, I=I)
     check_close_bf16_out(out_f64(out), ref, f"T={T} H={H} I={I} E={E} k={topk} bm={bm}")
+
+
+@pytest.mark.parametrize("T,E,topk", [(1, 8, 3), (2, 6, 4), (3, 5, 5), (4, 16, 2)])
+def test_forward_gemv_path_small(moe, T, E, topk):
+    """Decode blocks of at most 4 token rows with K a multiple of 512 take the
+    GEMV-shaped kernels; H=512, I=1024 keeps the oracle fast."""
+    H, I = 512, 1024
+    wl = synth.small(T=T, H=H, I=I, E=E, topk=topk, seed=40 + T)
+    out = run_layer(moe, wl, topk)
+    ids, w = oracle.route_topk(wl.logits, topk)
+    ref = oracle.moe_forward(wl.x, wl.w13, wl.w13_scale, wl.w2, wl.w2_scale, 0, ids, w, I=I)
+    check_close_bf16_out(out_f64(out), ref, f"gemv T={T} E={E} k={topk}")
 
 
 def test_forward_precomputed_routing_matches_oracle_inputs(moe):
