@@ -183,9 +183,11 @@ def stage1_kernel_name(T, bm, fmt, H, I, topk):
     """Which gate_up kernel the library launches for this shape (the rule of
     gemv_eligible / forward_stages in the C sources, restated for the label)."""
     rows = min(T, bm)
-    if (fmt == 0 and rows <= 4 and topk <= 16 and H <= 4096 and I <= 4096 and H % 512 == 0
-            and I % 512 == 0):
+    if (bm <= 32 and fmt == 0 and rows <= 4 and topk <= 16 and H <= 4096 and I <= 4096
+            and H % 512 == 0 and I % 512 == 0):
         return "stage1_gemv_kernel"
+    if fmt == 0 and bm == 32 and H % 256 == 0 and I % 256 == 0 and T * topk >= 1024:
+        return "prefill_kernel<1>"
     return "stage1_unit_kernel" if bm <= 32 else "stage1_stream_kernel"
 
 

@@ -86,7 +86,7 @@ moe_status moe_route_topk(const float* logits, int T, int E, int topk, int renor
 int64_t moe_align_sort_capacity(int T, int topk, int E, int block_m);
 
 /* Block size the forward works best with for this token count
- * (one of 16, 32, 64, 128). */
+ * (16 up to 16 tokens, else 32). */
 int moe_default_block_m(int T, int topk, int E);
 
 /* Group the P = T*topk (token, slot) pairs by expert for the grouped GEMMs
@@ -139,8 +139,9 @@ int64_t moe_a16w4_workspace_size(int T, int H, int I, int E, int topk, int block
  *   out           bf16 [T, H].
  *   workspace     device memory of moe_a16w4_workspace_size bytes.
  * Requirements: H % 32 == 0, I % 32 == 0, H >= 32, I >= 32, E >= 1,
- *   1 <= topk <= E, block_m in {16, 32, 64, 128, 256}; all pointers
- *   16-byte aligned (workspace 256-byte aligned).
+ *   1 <= topk <= E, block_m in {16, 32, 64} (128 and 256 are valid sort
+ *   sizes but give MOE_ERR_UNSUPPORTED here); all pointers 16-byte aligned
+ *   (workspace 256-byte aligned).
  * MXFP4 e8m0 bytes must be in [0, 254]; weights whose value overflows bf16
  * give unspecified results. */
 moe_status moe_a16w4_forward(const uint16_t* x, const uint8_t* w13, const void* w13_scale,

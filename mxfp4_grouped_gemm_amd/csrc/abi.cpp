@@ -46,7 +46,7 @@ int64_t capacity(int T, int topk, int E, int bm) {
 int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
 
 struct WsLayout {
-    int64_t h_off, h_bytes, y_off, y_bytes, total;
+    int64_t h_off, h_bytes, y_off, y_bytes, list_off, list_bytes, total;
 };
 
 WsLayout ws_layout(int T, int H, int I, int E, int topk, int bm) {
@@ -56,7 +56,9 @@ WsLayout ws_layout(int T, int H, int I, int E, int topk, int bm) {
     L.h_bytes = align_up(cap * I * 2, 256);
     L.y_off = L.h_off + L.h_bytes;
     L.y_bytes = align_up((int64_t)T * topk * H * 4, 256);
-    L.total = L.y_off + L.y_bytes;
+    L.list_off = L.y_off + L.y_bytes;
+    L.list_bytes = bm == 32 ? align_up(moe::prefill_list_bytes(cap), 256) : 0;
+    L.total = L.list_off + L.list_bytes;
     return L;
 }
 
@@ -75,8 +77,7 @@ int moe_default_block_m(int T, int topk, int E) {
     (void)topk;
     (void)E;
     if (T <= 16) return 16;
-    if (T <= 32) return 32;
-    return 64;
+    return 32;
 }
 
 moe_status moe_route_topk(const float* logits, int T, int E, int topk, int renormalize,
@@ -238,16 +239,24 @@ moe_status moe_a16w4_forward_stages(const uint16_t* x, const uint8_t* w13, const
     a.out = out;
     hipStream_t s = (hipStream_t)stream;
     moe_status st = MOE_OK;
+    // Kernel family per shape: GEMV waves for blocks of <= 4 token rows,
+    // the LDS-tiled MFMA kernels at prefill sizes, wave-per-tile MFMA
+    // kernels for other 16/32-row blocks, split-K workgroups for 64.
     const bool decode = block_m <= 32;
+    const bool gemv = decode && moe::gemv_eligible(a);
+    const bool prefill = !gemv && moe::prefill_eligible(a) && P >= moe::kPrefillMinPairs;
+    void* list = (char*)workspace + L.list_off;
     // The GEMV decode path combines inside its down launch.
-    const bool combined_in_down = decode && moe::gemv_eligible(a);
+    const bool combined_in_down = gemv;
     if (stages & MOE_STAGE_GATE_UP) {
-        st = hip_status(decode ? moe::launch_decode_stage(a, 1, s) : moe::launch_stage1(a, s),
+        st = hip_status(prefill ? moe::launch_prefill(a, 1, list, s)
+                        : decode ? moe::launch_decode_stage(a, 1, s) : moe::launch_stage1(a, s),
                         "moe_a16w4_forward (gate_up)");
         if (st != MOE_OK) return st;
     }
     if (stages & MOE_STAGE_DOWN) {
-        st = hip_status(decode ? moe::launch_decode_stage(a, 2, s) : moe::launch_stage2(a, s),
+        st = hip_status(prefill ? moe::launch_prefill(a, 2, list, s)
+                        : decode ? moe::launch_decode_stage(a, 2, s) : moe::launch_stage2(a, s),
                         "moe_a16w4_forward (down)");
         if (st != MOE_OK) return st;
     }

@@ -1,0 +1,360 @@
+// Prefill-sized grouped GEMMs (MXFP4 weights, bf16 MFMA).
+//
+// At prefill every expert holds on the order of a hundred token rows, so the
+// layer is a dense contraction and runs on v_mfma_f32_32x32x16_bf16. The
+// pages' two-stage MoE GEMM (the MXFP4-to-int4 pull request, Test plan) is
+// kept: stage 1 = gate_up GEMM + SwiGLU into h, stage 2 = down GEMM into y by
+// pair index, then the weighted combine.
+//
+// Work unit. The align/sort pads each expert segment to 32-row blocks. A
+// small kernel cuts every run of blocks of one expert into super-blocks of
+// at most 8 blocks (256 rows). A workgroup owns (super-block, N tile): its 4
+// waves share the super-block's activation rows through LDS, each wave owns
+// two 32-column weight blocks and all of the super-block's 32-row blocks, so
+// every decoded weight fragment feeds up to 8 MFMAs and the weight bytes of
+// an (expert, N tile) are read once from HBM.
+//  * Activations: 64-element K chunks; global loads run four chunks ahead
+//    in registers, then go to one of three LDS buffers (one barrier per
+//    chunk, and the next chunk's first MFMA operands are read before it). A row is 128 bytes and its 16-byte pieces are XOR-swizzled by
+//    (row/2)%8, so a 16-lane group of MFMA operand reads or of stores touches
+//    all 64 banks once. (Loads straight into LDS were tried: the compiler
+//    then waits for every outstanding load before each LDS read.)
+//  * Weights: lane (n = l%32, half = l/32) takes 16 bytes = one MX block of
+//    weight row n per chunk; the K order inside a chunk is permuted (half h
+//    covers elements 32h..32h+31 as four 8-element MFMA k-steps), and the
+//    activation operand reads use the same order, so the sums are unchanged.
+//    Four chunks of weights are in flight in a register ring; the e8m0 byte
+//    of each block rides with it. Decoding uses the scaled fp4 -> bf16
+//    converts (exact).
+//  * The super-block's row count (1..8 blocks) selects a specialisation of
+//    the main loop, so padding beyond the last 32-row block costs nothing.
+// Workgroups of one super-block sit on one XCD (consecutive workgroup ids go
+// round-robin over the 8 XCDs), so its activation rows stay in that L2.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace moe {
+
+namespace {
+
+constexpr int kPfThreads = 256;
+constexpr int kPfBlockRows = 32;   // align/sort block size this path expects
+constexpr int kPfMaxBlocks = 8;    // 32-row blocks per super-block
+constexpr int kPfChunk = 64;       // K elements per pipeline step
+constexpr int kPfRowBytes = kPfChunk * 2;
+constexpr int kPfABuf = kPfMaxBlocks * kPfBlockRows * kPfRowBytes;  // 32 KB
+constexpr int kPfABufs = 3;
+constexpr int kPfRing = 4;         // weight chunks in flight (loop unroll)
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+struct __attribute__((aligned(16))) PfShared {
+    uint8_t a[kPfABufs][kPfABuf];
+    int32_t rows[kPfMaxBlocks * kPfBlockRows];  // sorted_ids of the super-block
+};
+
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// Super-blocks: runs of consecutive blocks with the same expert, cut every
+// 8 blocks. One 1024-thread workgroup; list[i] = {expert, first row, blocks}.
+// Robust to any block order (a run is what it is, wherever it sits).
+__global__ __launch_bounds__(1024) void superblock_kernel(const int32_t* __restrict__ block_expert,
+                                                         int nblocks, int E, int4* __restrict__ list,
+                                                         int* __restrict__ count) {
+    __shared__ int wred[16];
+    __shared__ int carry_run, carry_cnt;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    if (tid == 0) {
+        carry_run = 0;
+        carry_cnt = 0;
+    }
+    __syncthreads();
+    for (int base = 0; base < nblocks; base += 1024) {
+        const int b = base + tid;
+        const int e = b < nblocks ? block_expert[b] : -1;
+        const bool run_start = b < nblocks && (b == 0 || block_expert[b - 1] != e);
+        // Inclusive max-scan of run starts: the first block of b's run.
+        int v = run_start ? b : -1;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int o = __shfl_up(v, off);
+            if (lane >= off) v = max(v, o);
+        }
+        if (lane == 63) wred[wv] = v;
+        __syncthreads();
+        int rs = carry_run;
+        for (int w = 0; w < wv; ++w) rs = max(rs, wred[w]);
+        rs = max(rs, v);
+        const bool start = (unsigned)e < (unsigned)E && ((b - rs) % kPfMaxBlocks) == 0;
+        // Inclusive count scan of super-block starts.
+        int c = start ? 1 : 0;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int o = __shfl_up(c, off);
+            if (lane >= off) c += o;
+        }
+        __syncthreads();
+        if (lane == 63) wred[wv] = c;
+        __syncthreads();
+        int cb = carry_cnt;
+        for (int w = 0; w < wv; ++w) cb += wred[w];
+        if (start) {
+            int nb = 1;
+            while (nb < kPfMaxBlocks && b + nb < nblocks && block_expert[b + nb] == e) ++nb;
+            list[cb + c - 1] = make_int4(e, b * kPfBlockRows, nb, 0);
+        }
+        __syncthreads();
+        if (tid == 1023) {
+            carry_run = rs;
+            carry_cnt = cb + c;
+        }
+        __syncthreads();
+    }
+    if (tid == 0) *count = carry_cnt;
+}
+
+// ---------------------------------------------------------------------------
+// Main loop of one (super-block, N tile), NB 32-row blocks.
+//   STAGE 1: A = x rows gathered by pair / topk, K = H; wave w owns gate
+//            columns n0+32w.. and the matching up columns; epilogue SwiGLU
+//            -> h[sorted row] (bf16).
+//   STAGE 2: A = h rows (contiguous), K = I; wave w owns columns
+//            n0+64w.. +64 of w2; epilogue y[pair] (fp32).
+template <int STAGE, int NB>
+__device__ __forceinline__ void pf_tile(const MoeGemmArgs& a, PfShared& sh, int e, int row0, int n0) {
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int P = a.T * a.topk;
+    const int K = STAGE == 1 ? a.H : a.I;
+    const int nchunks = K / kPfChunk;
+
+    // --- activations: thread t moves row 32i + t/8, logical piece t%8 of
+    // every 32-row block i; in LDS the piece sits at t%8 ^ ((row/2) % 8).
+    const int arow = tid >> 3;
+    const int apiece = tid & 7;
+    const uint32_t lds_w = (uint32_t)arow * kPfRowBytes + (uint32_t)((apiece ^ ((arow >> 1) & 7)) << 4);
+    rsrc_t ra;
+    uint32_t aoff[NB];
+    if (STAGE == 1) {
+        ra = make_rsrc(a.x, (uint32_t)((int64_t)a.T * a.H * 2));
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+            const int p = sh.rows[32 * i + arow];
+            aoff[i] = (p >= 0 && p < P) ? (uint32_t)(p / a.topk) * (uint32_t)(2 * a.H) + 16u * apiece : kOob;
+        }
+    } else {
+        ra = make_rsrc(a.h, (uint32_t)(a.cap * a.I * 2));
+#pragma unroll
+        for (int i = 0; i < NB; ++i)
+            aoff[i] = (uint32_t)(row0 + 32 * i + arow) * (uint32_t)(2 * a.I) + 16u * apiece;
+    }
+
+    // --- weight rows of this lane: block 0 / 1 of the wave.
+    const int half = lane >> 5;
+    const int nl = lane & 31;
+    int wrow[2];
+    rsrc_t rw, rs;
+    if (STAGE == 1) {
+        wrow[0] = n0 + 32 * w + nl;          // gate
+        wrow[1] = a.I + n0 + 32 * w + nl;    // up
+        const int64_t slab = 2 * (int64_t)a.I;
+        rw = make_rsrc(a.w13 + (int64_t)e * slab * (a.H / 2), (uint32_t)(slab * (a.H / 2)));
+        rs = make_rsrc((const uint8_t*)a.w13_scale + (int64_t)e * slab * (a.H / 32), (uint32_t)(slab * (a.H / 32)));
+    } else {
+        wrow[0] = n0 + 64 * w + nl;
+        wrow[1] = n0 + 64 * w + 32 + nl;
+        rw = make_rsrc(a.w2 + (int64_t)e * a.H * (a.I / 2), (uint32_t)((int64_t)a.H * (a.I / 2)));
+        rs = make_rsrc((const uint8_t*)a.w2_scale + (int64_t)e * a.H * (a.I / 32), (uint32_t)((int64_t)a.H * (a.I / 32)));
+    }
+    const uint32_t wo0 = (uint32_t)wrow[0] * (uint32_t)(K / 2) + 16u * half;
+    const uint32_t wo1 = (uint32_t)wrow[1] * (uint32_t)(K / 2) + 16u * half;
+    const uint32_t so0 = (uint32_t)wrow[0] * (uint32_t)(K / 32) + half;
+    const uint32_t so1 = (uint32_t)wrow[1] * (uint32_t)(K / 32) + half;
+
+    // Register rings: activations (global -> registers) four chunks ahead
+    // in two slots, weights four chunks ahead. Chunks past the end are
+    // issued with out-of-range offsets (zeros, no traffic).
+    u32x4 ar[2][NB];
+    u32x4 bw[kPfRing][2];
+    uint32_t bs[kPfRing][2];
+    auto issue_b = [&](int slot, int c) {
+        const bool ok = c < nchunks;
+        bw[slot][0] = bld16(rw, ok ? wo0 + 32u * c : kOob);
+        bw[slot][1] = bld16(rw, ok ? wo1 + 32u * c : kOob);
+        bs[slot][0] = __builtin_amdgcn_raw_buffer_load_b8(rs, ok ? so0 + 2u * c : kOob, 0, 0);
+        bs[slot][1] = __builtin_amdgcn_raw_buffer_load_b8(rs, ok ? so1 + 2u * c : kOob, 0, 0);
+    };
+    auto issue_a = [&](int slot, int c) {
+        const bool ok = c < nchunks;
+#pragma unroll
+        for (int i = 0; i < NB; ++i)
+            ar[slot][i] = bld16(ra, (ok && aoff[i] != kOob) ? aoff[i] + (uint32_t)(kPfRowBytes * c) : kOob);
+    };
+    auto store_a = [&](int slot, int buf) {
+#pragma unroll
+        for (int i = 0; i < NB; ++i)
+            *(u32x4*)(&sh.a[buf][32 * i * kPfRowBytes + lds_w]) = ar[slot][i];
+    };
+    // MFMA A operand from LDS: row 32i + nl, logical piece 4*half + s.
+    const int sw = (nl >> 1) & 7;
+    bf16x8 av[2][NB];
+    auto read_a = [&](int dst, int buf, int s) {
+        const uint8_t* base = sh.a[buf] + nl * kPfRowBytes + (((4 * half + s) ^ sw) << 4);
+#pragma unroll
+        for (int i = 0; i < NB; ++i) av[dst][i] = *(const bf16x8*)(base + 32 * i * kPfRowBytes);
+    };
+
+    f32x16 acc[NB][2];
+#pragma unroll
+    for (int i = 0; i < NB; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+
+    // Three LDS buffers: at step c, chunk c is read from buffer c%3, chunk
+    // c+1 already sits in buffer (c+1)%3 (so the first operands of the next
+    // step are read before the step's barrier) and chunk c+2 is stored into
+    // buffer (c+2)%3, the one chunk c-1 used.
+    issue_a(0, 0);
+    issue_a(1, 1);
+    issue_b(0, 0);
+    issue_b(1, 1);
+    issue_b(2, 2);
+    issue_b(3, 3);
+    store_a(0, 0);
+    issue_a(0, 2);
+    store_a(1, 1);
+    issue_a(1, 3);
+    __syncthreads();
+    read_a(0, 0, 0);
+
+    int buf = 0;  // chunk c's LDS buffer, c % 3
+    for (int c0 = 0; c0 < nchunks; c0 += kPfRing) {
+#pragma unroll
+        for (int u = 0; u < kPfRing; ++u) {
+            const int c = c0 + u;
+            const int buf1 = buf == 2 ? 0 : buf + 1;
+            const int buf2 = buf1 == 2 ? 0 : buf1 + 1;
+            store_a(u & 1, buf2);      // A(c+2)
+            issue_a(u & 1, c + 4);
+            const float sc0 = e8m0_scale_operand(bs[u][0]);
+            const float sc1 = e8m0_scale_operand(bs[u][1]);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                // operands of the next k-step (the next chunk's first one
+                // at s = 3) while this one runs
+                if (s < 3) read_a((s + 1) & 1, buf, s + 1);
+                else read_a(0, buf1, 0);
+                // Keep those reads ahead of this step's MFMAs (the scheduler
+                // otherwise sinks each read next to its use and the LDS
+                // latency lands between MFMAs).
+                __builtin_amdgcn_sched_barrier(0);
+                const bf16x8 b0 = mxfp4x8_to_bf16(bw[u][0][s], sc0);
+                const bf16x8 b1 = mxfp4x8_to_bf16(bw[u][1][s], sc1);
+#pragma unroll
+                for (int i = 0; i < NB; ++i) {
+                    acc[i][0] = mfma32(av[s & 1][i], b0, acc[i][0]);
+                    acc[i][1] = mfma32(av[s & 1][i], b1, acc[i][1]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            issue_b(u, c + 4);
+            __syncthreads();  // A(c+2) visible; buffer c%3 free for A(c+3)
+            buf = buf1;
+        }
+    }
+
+    // --- epilogue. acc[i][j][q]: row 32i + 8(q/4) + 4*half + q%4, column nl.
+    if (STAGE == 1) {
+        const int col = n0 + 32 * w + nl;
+#pragma unroll
+        for (int i = 0; i < NB; ++i) {
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                const int r = 32 * i + 8 * (q >> 2) + 4 * half + (q & 3);
+                a.h[(int64_t)(row0 + r) * a.I + col] = f32_to_bf16_bits(swiglu(acc[i][0][q], acc[i][1][q]));
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < NB; ++i)
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                const int r = 32 * i + 8 * (q >> 2) + 4 * half + (q & 3);
+                const int p = sh.rows[r];
+                if (p >= 0 && p < P) {
+                    float* yr = a.y + (int64_t)p * a.H + n0 + 64 * w + nl;
+                    yr[0] = acc[i][0][q];
+                    yr[32] = acc[i][1][q];
+                }
+            }
+    }
+}
+
+template <int STAGE>
+__global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(MoeGemmArgs a, const int4* __restrict__ list,
+                                                                const int* __restrict__ count, int ntiles) {
+    __shared__ PfShared sh;
+    // Workgroup id -> (super-block, N tile): ids go round-robin over the 8
+    // XCDs, so super-block s lives on XCD s % 8 with all of its N tiles.
+    const int b = blockIdx.x;
+    const int xcd = b & 7, j = b >> 3;
+    const int s = 8 * (j / ntiles) + xcd;
+    const int nt = j % ntiles;
+    if (s >= *count) return;
+    const int4 sb = list[s];
+    const int e = sb.x, row0 = sb.y, nb = sb.z;
+    for (int r = threadIdx.x; r < kPfMaxBlocks * kPfBlockRows; r += kPfThreads)
+        sh.rows[r] = r < nb * kPfBlockRows ? a.sorted_ids[row0 + r] : -1;
+    __syncthreads();
+    const int n0 = nt * (STAGE == 1 ? 128 : 256);
+    switch (nb) {
+        case 1: pf_tile<STAGE, 1>(a, sh, e, row0, n0); break;
+        case 2: pf_tile<STAGE, 2>(a, sh, e, row0, n0); break;
+        case 3: pf_tile<STAGE, 3>(a, sh, e, row0, n0); break;
+        case 4: pf_tile<STAGE, 4>(a, sh, e, row0, n0); break;
+        case 5: pf_tile<STAGE, 5>(a, sh, e, row0, n0); break;
+        case 6: pf_tile<STAGE, 6>(a, sh, e, row0, n0); break;
+        case 7: pf_tile<STAGE, 7>(a, sh, e, row0, n0); break;
+        default: pf_tile<STAGE, 8>(a, sh, e, row0, n0); break;
+    }
+}
+
+bool prefill_eligible(const MoeGemmArgs& a) {
+    return a.fmt == kFmtMxfp4 && a.bm == kPfBlockRows && a.H % 256 == 0 && a.I % 256 == 0 &&
+           a.cap * a.I * 2 < 0x7fff0000LL && (int64_t)a.T * a.H * 2 < 0x7fff0000LL &&
+           (int64_t)2 * a.I * (a.H / 2) < 0x7fff0000LL;
+}
+
+int64_t prefill_list_bytes(int64_t cap) { return (cap / kPfBlockRows + 1) * 16 + 256; }
+
+hipError_t launch_prefill(const MoeGemmArgs& a, int stage, void* list_ws, hipStream_t s) {
+    int4* list = (int4*)list_ws;
+    const int64_t nblocks = a.cap / kPfBlockRows;
+    int* count = (int*)(list + nblocks);
+    if (stage == 1)
+        hipLaunchKernelGGL(superblock_kernel, dim3(1), dim3(1024), 0, s, a.block_expert, (int)nblocks, a.E,
+                           list, count);
+    // Super-blocks: sum over experts of ceil(rows / 256) <= P / 256 + min(E, P) + 1.
+    const int64_t P = (int64_t)a.T * a.topk;
+    int64_t sbound = P / (kPfMaxBlocks * kPfBlockRows) + (P < a.E ? P : a.E) + 1;
+    if (sbound > nblocks) sbound = nblocks;
+    const int ntiles = stage == 1 ? a.I / 128 : a.H / 256;
+    const int64_t grid = 8 * ((sbound + 7) / 8) * ntiles;
+    if (stage == 1)
+        hipLaunchKernelGGL(prefill_kernel<1>, dim3((unsigned)grid), dim3(kPfThreads), 0, s, a, list, count, ntiles);
+    else
+        hipLaunchKernelGGL(prefill_kernel<2>, dim3((unsigned)grid), dim3(kPfThreads), 0, s, a, list, count, ntiles);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -231,6 +231,30 @@ def test_forward_gemv_path_small(moe, T, E, topk):
     check_close_bf16_out(out_f64(out), ref, f"gemv T={T} E={E} k={topk}")
 
 
+@pytest.mark.parametrize("T,H,I,E,topk,hot", [
+    (256, 512, 512, 8, 4, 0),    # ~128 rows per expert: 4-block super-blocks
+    (512, 768, 256, 4, 3, 0),    # ~384 rows per expert: two super-blocks each
+    (300, 256, 768, 16, 5, 0),   # ragged T, 1..4-block super-blocks
+    (400, 512, 256, 32, 4, 4),   # skewed: 4 hot experts take most pairs
+])
+def test_forward_prefill_path(moe, T, H, I, E, topk, hot):
+    """At least 1024 pairs with H and I multiples of 256 take the LDS-tiled
+    MFMA kernels (32-row blocks cut into super-blocks of up to 256 rows);
+    every token is compared."""
+    wl = synth.small(T=T, H=H, I=I, E=E, topk=topk, seed=7 * T + E, hot=hot)
+    assert moe.moe_default_block_m(T, topk, E) == 32
+    out = run_layer(moe, wl, topk)
+    ids, w = oracle.route_topk(wl.logits, topk)
+    ref = oracle.moe_forward(wl.x, wl.w13, wl.w13_scale, wl.w2, wl.w2_scale, 0, ids, w, I=I)
+    # Every output of these shapes is compared; the largest are ~10 RMS, so
+    # the bf16 rounding of the output alone reaches ~2e-2 RMS: bar + rounding.
+    got = out_f64(out)
+    check_close_bf16_out(got, ref, f"prefill T={T} H={H} I={I} E={E} k={topk} hot={hot}")
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    print(f"prefill T={T} E={E}: max|err| {np.abs(got - ref).max() / rms:.2e} of RMS, "
+          f"max|ref| {np.abs(ref).max() / rms:.1f} RMS")
+
+
 def test_forward_precomputed_routing_matches_oracle_inputs(moe):
     """apply()-style call: routing from the oracle fed to the GPU forward."""
     wl = synth.small(T=9, H=256, I=128, E=8, topk=3, seed=31)
