@@ -235,36 +235,60 @@ __device__ __forceinline__ void pf_tile(const MoeGemmArgs& a, PfShared& sh, int 
     issue_a(1, 3);
     __syncthreads();
     read_a(0, 0, 0);
+    // Decoded weights of the current k-step; the next step's are decoded
+    // while this step's MFMAs run.
+    bf16x8 b0 = mxfp4x8_to_bf16(bw[0][0][0], e8m0_scale_operand(bs[0][0]));
+    bf16x8 b1 = mxfp4x8_to_bf16(bw[0][1][0], e8m0_scale_operand(bs[0][1]));
 
     int buf = 0;  // chunk c's LDS buffer, c % 3
     for (int c0 = 0; c0 < nchunks; c0 += kPfRing) {
 #pragma unroll
         for (int u = 0; u < kPfRing; ++u) {
             const int c = c0 + u;
+            const int un = (u + 1) % kPfRing;
             const int buf1 = buf == 2 ? 0 : buf + 1;
             const int buf2 = buf1 == 2 ? 0 : buf1 + 1;
-            store_a(u & 1, buf2);      // A(c+2)
-            issue_a(u & 1, c + 4);
             const float sc0 = e8m0_scale_operand(bs[u][0]);
             const float sc1 = e8m0_scale_operand(bs[u][1]);
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-                // operands of the next k-step (the next chunk's first one
-                // at s = 3) while this one runs
-                if (s < 3) read_a((s + 1) & 1, buf, s + 1);
-                else read_a(0, buf1, 0);
-                // Keep those reads ahead of this step's MFMAs (the scheduler
-                // otherwise sinks each read next to its use and the LDS
-                // latency lands between MFMAs).
-                __builtin_amdgcn_sched_barrier(0);
-                const bf16x8 b0 = mxfp4x8_to_bf16(bw[u][0][s], sc0);
-                const bf16x8 b1 = mxfp4x8_to_bf16(bw[u][1][s], sc1);
+                // Operands of the next k-step (the next chunk's first at s = 3).
+                bf16x8 n0, n1;
+                if (s < 3) {
+                    read_a((s + 1) & 1, buf, s + 1);
+                    n0 = mxfp4x8_to_bf16(bw[u][0][s + 1], sc0);
+                    n1 = mxfp4x8_to_bf16(bw[u][1][s + 1], sc1);
+                } else {
+                    read_a(0, buf1, 0);
+                    n0 = mxfp4x8_to_bf16(bw[un][0][0], e8m0_scale_operand(bs[un][0]));
+                    n1 = mxfp4x8_to_bf16(bw[un][1][0], e8m0_scale_operand(bs[un][1]));
+                }
+                if (s == 0) {
+                    store_a(u & 1, buf2);  // A(c+2)
+                    issue_a(u & 1, c + 4);
+                }
 #pragma unroll
                 for (int i = 0; i < NB; ++i) {
                     acc[i][0] = mfma32(av[s & 1][i], b0, acc[i][0]);
                     acc[i][1] = mfma32(av[s & 1][i], b1, acc[i][1]);
                 }
-                __builtin_amdgcn_sched_barrier(0);
+                // Interleave: each MFMA pair is followed by one operand read
+                // and a couple of converts for the next step (and at s = 0 by
+                // the activation stores and loads), so the matrix core is fed
+                // while the VALU and LDS work proceeds.
+#pragma unroll
+                for (int i = 0; i < NB; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+                    if (s == 0) {
+                        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
+                        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
+                    }
+                    __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // VALU
+                }
+                __builtin_amdgcn_sched_barrier(0);  // one k-step per scheduling region
+                b0 = n0;
+                b1 = n1;
             }
             issue_b(u, c + 4);
             __syncthreads();  // A(c+2) visible; buffer c%3 free for A(c+3)
@@ -273,29 +297,35 @@ __device__ __forceinline__ void pf_tile(const MoeGemmArgs& a, PfShared& sh, int 
     }
 
     // --- epilogue. acc[i][j][q]: row 32i + 8(q/4) + 4*half + q%4, column nl.
+    // For a fixed (i, q) the wave holds two rows of 32 consecutive columns,
+    // so one 2- or 4-byte store per lane writes two contiguous segments; the
+    // row offset is wave-uniform and goes in the scalar offset.
     if (STAGE == 1) {
-        const int col = n0 + 32 * w + nl;
+        const rsrc_t rh = make_rsrc(a.h, (uint32_t)(a.cap * a.I * 2));
+        const uint32_t vbase = ((uint32_t)(row0 + 4 * half) * (uint32_t)a.I + (uint32_t)(n0 + 32 * w + nl)) * 2u;
 #pragma unroll
-        for (int i = 0; i < NB; ++i) {
+        for (int i = 0; i < NB; ++i)
 #pragma unroll
             for (int q = 0; q < 16; ++q) {
-                const int r = 32 * i + 8 * (q >> 2) + 4 * half + (q & 3);
-                a.h[(int64_t)(row0 + r) * a.I + col] = f32_to_bf16_bits(swiglu(acc[i][0][q], acc[i][1][q]));
+                const uint32_t soff = (uint32_t)(32 * i + 8 * (q >> 2) + (q & 3)) * (uint32_t)(2 * a.I);
+                __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_bits(swiglu_fast(acc[i][0][q], acc[i][1][q])),
+                                                      rh, vbase, soff, 0);
             }
-            __builtin_amdgcn_sched_barrier(0);
-        }
     } else {
+        const rsrc_t ry = make_rsrc(a.y, (uint32_t)((int64_t)P * a.H * 4));
+        const uint32_t col4 = (uint32_t)(n0 + 64 * w + nl) * 4u;
 #pragma unroll
         for (int i = 0; i < NB; ++i)
 #pragma unroll
             for (int q = 0; q < 16; ++q) {
                 const int r = 32 * i + 8 * (q >> 2) + 4 * half + (q & 3);
                 const int p = sh.rows[r];
-                if (p >= 0 && p < P) {
-                    float* yr = a.y + (int64_t)p * a.H + n0 + 64 * w + nl;
-                    yr[0] = acc[i][0][q];
-                    yr[32] = acc[i][1][q];
-                }
+                // Padding rows get an out-of-range offset: the store is dropped.
+                const uint32_t off = (p >= 0 && p < P) ? (uint32_t)p * (uint32_t)(4 * a.H) + col4 : kOob;
+                // The store builtin takes integer data. (A bit_cast of the vector
+                // element was folded to element 0 by the compiler.)
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][0][q]), ry, off, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][1][q]), ry, off, 128, 0);
             }
     }
 }
@@ -331,6 +361,7 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(MoeGemmArgs a, c
 
 bool prefill_eligible(const MoeGemmArgs& a) {
     return a.fmt == kFmtMxfp4 && a.bm == kPfBlockRows && a.H % 256 == 0 && a.I % 256 == 0 &&
+           (int64_t)a.T * a.topk * a.H * 4 < 0x7fff0000LL &&
            a.cap * a.I * 2 < 0x7fff0000LL && (int64_t)a.T * a.H * 2 < 0x7fff0000LL &&
            (int64_t)2 * a.I * (a.H / 2) < 0x7fff0000LL;
 }
