@@ -44,13 +44,19 @@ constexpr int kPfChunk = 64;       // K elements per pipeline step
 constexpr int kPfRowBytes = kPfChunk * 2;
 constexpr int kPfABuf = kPfMaxBlocks * kPfBlockRows * kPfRowBytes;  // 32 KB
 constexpr int kPfABufs = 3;
-constexpr int kPfRing = 4;         // weight chunks in flight (loop unroll)
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
+// Weights are staged per wave, four chunks (256 K elements) at a time: the
+// wave's 64 weight rows x 128 bytes of codes (swizzled like the activation
+// tile) and 64 rows x 8 e8m0 bytes.
+constexpr int kPfWRows = 64;
+constexpr int kPfStage = 4;  // chunks per weight stage
 struct __attribute__((aligned(16))) PfShared {
     uint8_t a[kPfABufs][kPfABuf];
+    uint8_t b[4][kPfWRows * 128];
+    uint8_t bs[4][kPfWRows * 8];
     int32_t rows[kPfMaxBlocks * kPfBlockRows];  // sorted_ids of the super-block
 };
 
@@ -156,41 +162,76 @@ __device__ __forceinline__ void pf_tile(const MoeGemmArgs& a, PfShared& sh, int 
             aoff[i] = (uint32_t)(row0 + 32 * i + arow) * (uint32_t)(2 * a.I) + 16u * apiece;
     }
 
-    // --- weight rows of this lane: block 0 / 1 of the wave.
+    // --- weights. Staging row r (0..63) of wave w: block r / 32 of the wave
+    // (stage 1: gate columns n0+32w.., then the matching up rows; stage 2:
+    // columns n0+64w..+64), row r % 32 of it.
     const int half = lane >> 5;
     const int nl = lane & 31;
-    int wrow[2];
     rsrc_t rw, rs;
+    auto grow = [&](int r) -> uint32_t {
+        if (STAGE == 1) return (uint32_t)((r < 32 ? 0 : a.I) + n0 + 32 * w + (r & 31));
+        return (uint32_t)(n0 + 64 * w + r);
+    };
     if (STAGE == 1) {
-        wrow[0] = n0 + 32 * w + nl;          // gate
-        wrow[1] = a.I + n0 + 32 * w + nl;    // up
         const int64_t slab = 2 * (int64_t)a.I;
         rw = make_rsrc(a.w13 + (int64_t)e * slab * (a.H / 2), (uint32_t)(slab * (a.H / 2)));
         rs = make_rsrc((const uint8_t*)a.w13_scale + (int64_t)e * slab * (a.H / 32), (uint32_t)(slab * (a.H / 32)));
     } else {
-        wrow[0] = n0 + 64 * w + nl;
-        wrow[1] = n0 + 64 * w + 32 + nl;
         rw = make_rsrc(a.w2 + (int64_t)e * a.H * (a.I / 2), (uint32_t)((int64_t)a.H * (a.I / 2)));
         rs = make_rsrc((const uint8_t*)a.w2_scale + (int64_t)e * a.H * (a.I / 32), (uint32_t)((int64_t)a.H * (a.I / 32)));
     }
-    const uint32_t wo0 = (uint32_t)wrow[0] * (uint32_t)(K / 2) + 16u * half;
-    const uint32_t wo1 = (uint32_t)wrow[1] * (uint32_t)(K / 2) + 16u * half;
-    const uint32_t so0 = (uint32_t)wrow[0] * (uint32_t)(K / 32) + half;
-    const uint32_t so1 = (uint32_t)wrow[1] * (uint32_t)(K / 32) + half;
-
-    // Register rings: activations (global -> registers) four chunks ahead
-    // in two slots, weights four chunks ahead. Chunks past the end are
-    // issued with out-of-range offsets (zeros, no traffic).
-    u32x4 ar[2][NB];
-    u32x4 bw[kPfRing][2];
-    uint32_t bs[kPfRing][2];
-    auto issue_b = [&](int slot, int c) {
-        const bool ok = c < nchunks;
-        bw[slot][0] = bld16(rw, ok ? wo0 + 32u * c : kOob);
-        bw[slot][1] = bld16(rw, ok ? wo1 + 32u * c : kOob);
-        bs[slot][0] = __builtin_amdgcn_raw_buffer_load_b8(rs, ok ? so0 + 2u * c : kOob, 0, 0);
-        bs[slot][1] = __builtin_amdgcn_raw_buffer_load_b8(rs, ok ? so1 + 2u * c : kOob, 0, 0);
+    // Stage loads: instruction j moves rows 8j..8j+7, eight lanes (128
+    // contiguous bytes, one cache line) per row; the scale bytes of row
+    // `lane` come with one 8-byte load.
+    uint32_t boff[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) boff[j] = grow(8 * j + (lane >> 3)) * (uint32_t)(K / 2) + 16u * (lane & 7);
+    const uint32_t soff = grow(lane) * (uint32_t)(K / 32);
+    const int nstages = nchunks / kPfStage;
+    u32x4 braw[8];
+    u32x2 sraw;
+    auto issue_bstage = [&](int st) {
+        const bool ok = st < nstages;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) braw[j] = bld16(rw, ok ? boff[j] + 128u * st : kOob);
+        sraw = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, ok ? soff + 8u * st : kOob, 0, 0));
     };
+    uint8_t* const wl = sh.b[w];
+    uint8_t* const sl = sh.bs[w];
+    auto store_bstage = [&]() {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int r = 8 * j + (lane >> 3);
+            *(u32x4*)(wl + r * 128 + (((lane & 7) ^ ((r >> 1) & 7)) << 4)) = braw[j];
+        }
+        *(u32x2*)(sl + lane * 8) = sraw;
+    };
+    // MFMA B operand of chunk j of the stage, block nb: row 32nb + nl,
+    // logical piece 2j + half (16 bytes = one MX block of 32 codes).
+    auto read_bchunk = [&](u32x4 (&dst)[2], int j) {
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+            const int r = 32 * nb + nl;
+            dst[nb] = *(const u32x4*)(wl + r * 128 + (((2 * j + half) ^ ((r >> 1) & 7)) << 4));
+        }
+    };
+    auto read_scales = [&](u32x2 (&dst)[2]) {
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) dst[nb] = *(const u32x2*)(sl + (32 * nb + nl) * 8);
+    };
+    // e8m0 byte of chunk j (block 2j + half of the stage) as a scale operand.
+    auto scale_of = [&](const u32x2& w8, int j) -> float {
+        const uint32_t word = j < 2 ? w8[0] : w8[1];
+        return e8m0_scale_operand((word >> (16 * (j & 1) + 8 * half)) & 0xffu);
+    };
+
+    // Activation ring: chunk k lives in slot k % DA from its load (DA chunks
+    // before it is stored to LDS) to that store. Vector-memory counts retire
+    // in order, so this depth is the latency budget of every load; it is as
+    // deep as the registers allow. Chunks past the end are issued with
+    // out-of-range offsets (zeros, no traffic).
+    constexpr int DA = NB <= 6 ? 4 : 2;
+    u32x4 ar[DA][NB];
     auto issue_a = [&](int slot, int c) {
         const bool ok = c < nchunks;
 #pragma unroll
@@ -219,70 +260,87 @@ __device__ __forceinline__ void pf_tile(const MoeGemmArgs& a, PfShared& sh, int 
 #pragma unroll
             for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
 
-    // Three LDS buffers: at step c, chunk c is read from buffer c%3, chunk
-    // c+1 already sits in buffer (c+1)%3 (so the first operands of the next
-    // step are read before the step's barrier) and chunk c+2 is stored into
-    // buffer (c+2)%3, the one chunk c-1 used.
+    // Activations: three LDS buffers; at step c, chunk c is read from buffer
+    // c%3, chunk c+1 already sits in buffer (c+1)%3 (so the first operands of
+    // the next step are read before the step's barrier) and chunk c+2 is
+    // stored into buffer (c+2)%3, the one chunk c-1 used.
+    // Weights: stage t (chunks 4t..4t+3) is written to the wave's LDS in
+    // chunk 4t-2, after the last read of stage t-1 (chunk 4t-1's operands,
+    // read one chunk ahead); stage t+1 is then loaded into the registers.
     issue_a(0, 0);
     issue_a(1, 1);
-    issue_b(0, 0);
-    issue_b(1, 1);
-    issue_b(2, 2);
-    issue_b(3, 3);
+    issue_bstage(0);
     store_a(0, 0);
-    issue_a(0, 2);
     store_a(1, 1);
-    issue_a(1, 3);
+    store_bstage();
+    issue_bstage(1);
+#pragma unroll
+    for (int k = 2; k < 2 + DA; ++k) issue_a(k % DA, k);
     __syncthreads();
     read_a(0, 0, 0);
+    u32x4 bcur[2], bnext[2];
+    u32x2 scur[2], snext[2];
+    read_scales(scur);
+    read_bchunk(bcur, 0);
     // Decoded weights of the current k-step; the next step's are decoded
     // while this step's MFMAs run.
-    bf16x8 b0 = mxfp4x8_to_bf16(bw[0][0][0], e8m0_scale_operand(bs[0][0]));
-    bf16x8 b1 = mxfp4x8_to_bf16(bw[0][1][0], e8m0_scale_operand(bs[0][1]));
+    bf16x8 b0 = mxfp4x8_to_bf16(bcur[0][0], scale_of(scur[0], 0));
+    bf16x8 b1 = mxfp4x8_to_bf16(bcur[1][0], scale_of(scur[1], 0));
 
     int buf = 0;  // chunk c's LDS buffer, c % 3
-    for (int c0 = 0; c0 < nchunks; c0 += kPfRing) {
+    for (int c0 = 0; c0 < nchunks; c0 += kPfStage) {
 #pragma unroll
-        for (int u = 0; u < kPfRing; ++u) {
+        for (int u = 0; u < kPfStage; ++u) {
             const int c = c0 + u;
-            const int un = (u + 1) % kPfRing;
             const int buf1 = buf == 2 ? 0 : buf + 1;
             const int buf2 = buf1 == 2 ? 0 : buf1 + 1;
-            const float sc0 = e8m0_scale_operand(bs[u][0]);
-            const float sc1 = e8m0_scale_operand(bs[u][1]);
+            const float sc0 = scale_of(scur[0], u);
+            const float sc1 = scale_of(scur[1], u);
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
+                if (s == 0) {
+                    // next chunk's weight operands (and, at the stage's last
+                    // chunk, the next stage's scales)
+                    if (u < 3) read_bchunk(bnext, u + 1);
+                    else {
+                        read_bchunk(bnext, 0);
+                        read_scales(snext);
+                    }
+                    store_a((u + 2) % DA, buf2);  // A(c+2)
+                    issue_a((u + 2) % DA, c + 2 + DA);
+                    if (u == 2) {  // stage c0/4 + 1 into LDS, load the one after
+                        store_bstage();
+                        issue_bstage(c0 / kPfStage + 2);
+                    }
+                }
                 // Operands of the next k-step (the next chunk's first at s = 3).
                 bf16x8 n0, n1;
                 if (s < 3) {
                     read_a((s + 1) & 1, buf, s + 1);
-                    n0 = mxfp4x8_to_bf16(bw[u][0][s + 1], sc0);
-                    n1 = mxfp4x8_to_bf16(bw[u][1][s + 1], sc1);
+                    n0 = mxfp4x8_to_bf16(bcur[0][s + 1], sc0);
+                    n1 = mxfp4x8_to_bf16(bcur[1][s + 1], sc1);
                 } else {
                     read_a(0, buf1, 0);
-                    n0 = mxfp4x8_to_bf16(bw[un][0][0], e8m0_scale_operand(bs[un][0]));
-                    n1 = mxfp4x8_to_bf16(bw[un][1][0], e8m0_scale_operand(bs[un][1]));
-                }
-                if (s == 0) {
-                    store_a(u & 1, buf2);  // A(c+2)
-                    issue_a(u & 1, c + 4);
+                    const u32x2* sn = u < 3 ? scur : snext;
+                    n0 = mxfp4x8_to_bf16(bnext[0][0], scale_of(sn[0], (u + 1) & 3));
+                    n1 = mxfp4x8_to_bf16(bnext[1][0], scale_of(sn[1], (u + 1) & 3));
                 }
 #pragma unroll
                 for (int i = 0; i < NB; ++i) {
                     acc[i][0] = mfma32(av[s & 1][i], b0, acc[i][0]);
                     acc[i][1] = mfma32(av[s & 1][i], b1, acc[i][1]);
                 }
-                // Interleave: each MFMA pair is followed by one operand read
+                // Interleave: each MFMA pair is followed by an operand read
                 // and a couple of converts for the next step (and at s = 0 by
-                // the activation stores and loads), so the matrix core is fed
-                // while the VALU and LDS work proceeds.
+                // the stores and loads), so the matrix core is fed while the
+                // VALU and LDS work proceeds.
 #pragma unroll
                 for (int i = 0; i < NB; ++i) {
                     __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
                     __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
                     if (s == 0) {
-                        __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
-                        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
+                        __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);  // DS write
+                        __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);  // VMEM read
                     }
                     __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // VALU
                 }
@@ -290,7 +348,12 @@ __device__ __forceinline__ void pf_tile(const MoeGemmArgs& a, PfShared& sh, int 
                 b0 = n0;
                 b1 = n1;
             }
-            issue_b(u, c + 4);
+            bcur[0] = bnext[0];
+            bcur[1] = bnext[1];
+            if (u == 3) {
+                scur[0] = snext[0];
+                scur[1] = snext[1];
+            }
             __syncthreads();  // A(c+2) visible; buffer c%3 free for A(c+3)
             buf = buf1;
         }
