@@ -179,15 +179,16 @@ def measured_traffic(workload, kernel):
     return rec["hbm_bytes_per_launch"]
 
 
-def stage1_kernel_name(T, bm, fmt, H, I, topk):
+def stage1_kernel_name(T, bm, fmt, H, I, topk, E):
     """Which gate_up kernel the library launches for this shape (the rule of
     gemv_eligible / forward_stages in the C sources, restated for the label)."""
     rows = min(T, bm)
     if (bm <= 32 and fmt == 0 and rows <= 4 and topk <= 16 and H <= 4096 and I <= 4096
             and H % 512 == 0 and I % 512 == 0):
         return "stage1_gemv_kernel"
-    if fmt == 0 and bm == 32 and H % 256 == 0 and I % 256 == 0 and T * topk >= 1024:
-        return "prefill_kernel<1>"
+    P = T * topk
+    if fmt == 0 and bm == 32 and H % 256 == 0 and I % 256 == 0 and P >= 32:
+        return "prefill_kernel<1, 2>" if P <= 48 * min(P, E) else "prefill_kernel<1, 8>"
     return "stage1_unit_kernel" if bm <= 32 else "stage1_stream_kernel"
 
 
@@ -335,7 +336,7 @@ def main():
         ach = stage1_bytes / s1_sec / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": None}
-    kname = stage1_kernel_name(T, layers[0].bm, fmt, H, I, k)
+    kname = stage1_kernel_name(T, layers[0].bm, fmt, H, I, k, E)
     roof["traffic"] = measured_traffic(args.workload, kname)
     roof["kernel"] = kname + " (grouped gate_up GEMM + SwiGLU)"
     roof["avg_us"] = round(s1_us, 2)

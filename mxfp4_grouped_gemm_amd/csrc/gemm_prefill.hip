@@ -39,10 +39,10 @@ namespace {
 
 constexpr int kPfThreads = 256;
 constexpr int kPfBlockRows = 32;   // align/sort block size this path expects
-constexpr int kPfMaxBlocks = 8;    // 32-row blocks per super-block
+constexpr int kPfMaxBlocks = 8;    // 32-row blocks per super-block (prefill sizes)
+constexpr int kPfMaxBlocksSmall = 2;  // the same when experts hold few rows
 constexpr int kPfChunk = 64;       // K elements per pipeline step
 constexpr int kPfRowBytes = kPfChunk * 2;
-constexpr int kPfABuf = kPfMaxBlocks * kPfBlockRows * kPfRowBytes;  // 32 KB
 constexpr int kPfABufs = 3;
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -53,11 +53,12 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 // tile) and 64 rows x 8 e8m0 bytes.
 constexpr int kPfWRows = 64;
 constexpr int kPfStage = 4;  // chunks per weight stage
+template <int NBMAX>
 struct __attribute__((aligned(16))) PfShared {
-    uint8_t a[kPfABufs][kPfABuf];
+    uint8_t a[kPfABufs][NBMAX * kPfBlockRows * kPfRowBytes];
     uint8_t b[4][kPfWRows * 128];
     uint8_t bs[4][kPfWRows * 8];
-    int32_t rows[kPfMaxBlocks * kPfBlockRows];  // sorted_ids of the super-block
+    int32_t rows[NBMAX * kPfBlockRows];  // sorted_ids of the super-block
 };
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
@@ -68,10 +69,10 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 
 // ---------------------------------------------------------------------------
 // Super-blocks: runs of consecutive blocks with the same expert, cut every
-// 8 blocks. One 1024-thread workgroup; list[i] = {expert, first row, blocks}.
+// maxb blocks. One 1024-thread workgroup; list[i] = {expert, first row, blocks}.
 // Robust to any block order (a run is what it is, wherever it sits).
 __global__ __launch_bounds__(1024) void superblock_kernel(const int32_t* __restrict__ block_expert,
-                                                         int nblocks, int E, int4* __restrict__ list,
+                                                         int nblocks, int E, int maxb, int4* __restrict__ list,
                                                          int* __restrict__ count) {
     __shared__ int wred[16];
     __shared__ int carry_run, carry_cnt;
@@ -97,7 +98,7 @@ __global__ __launch_bounds__(1024) void superblock_kernel(const int32_t* __restr
         int rs = carry_run;
         for (int w = 0; w < wv; ++w) rs = max(rs, wred[w]);
         rs = max(rs, v);
-        const bool start = (unsigned)e < (unsigned)E && ((b - rs) % kPfMaxBlocks) == 0;
+        const bool start = (unsigned)e < (unsigned)E && ((b - rs) % maxb) == 0;
         // Inclusive count scan of super-block starts.
         int c = start ? 1 : 0;
 #pragma unroll
@@ -112,7 +113,7 @@ __global__ __launch_bounds__(1024) void superblock_kernel(const int32_t* __restr
         for (int w = 0; w < wv; ++w) cb += wred[w];
         if (start) {
             int nb = 1;
-            while (nb < kPfMaxBlocks && b + nb < nblocks && block_expert[b + nb] == e) ++nb;
+            while (nb < maxb && b + nb < nblocks && block_expert[b + nb] == e) ++nb;
             list[cb + c - 1] = make_int4(e, b * kPfBlockRows, nb, 0);
         }
         __syncthreads();
@@ -132,8 +133,8 @@ __global__ __launch_bounds__(1024) void superblock_kernel(const int32_t* __restr
 //            -> h[sorted row] (bf16).
 //   STAGE 2: A = h rows (contiguous), K = I; wave w owns columns
 //            n0+64w.. +64 of w2; epilogue y[pair] (fp32).
-template <int STAGE, int NB>
-__device__ __forceinline__ void pf_tile(const MoeGemmArgs& a, PfShared& sh, int e, int row0, int n0) {
+template <int STAGE, int NB, int NBMAX>
+__device__ __forceinline__ void pf_tile(const MoeGemmArgs& a, PfShared<NBMAX>& sh, int e, int row0, int n0) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -393,10 +394,12 @@ __device__ __forceinline__ void pf_tile(const MoeGemmArgs& a, PfShared& sh, int 
     }
 }
 
-template <int STAGE>
-__global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(MoeGemmArgs a, const int4* __restrict__ list,
-                                                                const int* __restrict__ count, int ntiles) {
-    __shared__ PfShared sh;
+template <int STAGE, int NBMAX>
+__global__ __launch_bounds__(kPfThreads, NBMAX <= 2 ? 2 : 1) void prefill_kernel(MoeGemmArgs a,
+                                                                               const int4* __restrict__ list,
+                                                                               const int* __restrict__ count,
+                                                                               int ntiles) {
+    __shared__ PfShared<NBMAX> sh;
     // Workgroup id -> (super-block, N tile): ids go round-robin over the 8
     // XCDs, so super-block s lives on XCD s % 8 with all of its N tiles.
     const int b = blockIdx.x;
@@ -406,19 +409,24 @@ __global__ __launch_bounds__(kPfThreads, 1) void prefill_kernel(MoeGemmArgs a, c
     if (s >= *count) return;
     const int4 sb = list[s];
     const int e = sb.x, row0 = sb.y, nb = sb.z;
-    for (int r = threadIdx.x; r < kPfMaxBlocks * kPfBlockRows; r += kPfThreads)
+    for (int r = threadIdx.x; r < NBMAX * kPfBlockRows; r += kPfThreads)
         sh.rows[r] = r < nb * kPfBlockRows ? a.sorted_ids[row0 + r] : -1;
     __syncthreads();
     const int n0 = nt * (STAGE == 1 ? 128 : 256);
-    switch (nb) {
-        case 1: pf_tile<STAGE, 1>(a, sh, e, row0, n0); break;
-        case 2: pf_tile<STAGE, 2>(a, sh, e, row0, n0); break;
-        case 3: pf_tile<STAGE, 3>(a, sh, e, row0, n0); break;
-        case 4: pf_tile<STAGE, 4>(a, sh, e, row0, n0); break;
-        case 5: pf_tile<STAGE, 5>(a, sh, e, row0, n0); break;
-        case 6: pf_tile<STAGE, 6>(a, sh, e, row0, n0); break;
-        case 7: pf_tile<STAGE, 7>(a, sh, e, row0, n0); break;
-        default: pf_tile<STAGE, 8>(a, sh, e, row0, n0); break;
+    if constexpr (NBMAX <= 2) {
+        if (nb == 1) pf_tile<STAGE, 1>(a, sh, e, row0, n0);
+        else pf_tile<STAGE, 2>(a, sh, e, row0, n0);
+    } else {
+        switch (nb) {
+            case 1: pf_tile<STAGE, 1>(a, sh, e, row0, n0); break;
+            case 2: pf_tile<STAGE, 2>(a, sh, e, row0, n0); break;
+            case 3: pf_tile<STAGE, 3>(a, sh, e, row0, n0); break;
+            case 4: pf_tile<STAGE, 4>(a, sh, e, row0, n0); break;
+            case 5: pf_tile<STAGE, 5>(a, sh, e, row0, n0); break;
+            case 6: pf_tile<STAGE, 6>(a, sh, e, row0, n0); break;
+            case 7: pf_tile<STAGE, 7>(a, sh, e, row0, n0); break;
+            default: pf_tile<STAGE, 8>(a, sh, e, row0, n0); break;
+        }
     }
 }
 
@@ -435,19 +443,30 @@ hipError_t launch_prefill(const MoeGemmArgs& a, int stage, void* list_ws, hipStr
     int4* list = (int4*)list_ws;
     const int64_t nblocks = a.cap / kPfBlockRows;
     int* count = (int*)(list + nblocks);
+    // Few rows per expert (decode batches): 64-row super-blocks and a small
+    // LDS footprint, so two workgroups share a CU and keep more weight bytes
+    // in flight. Both stages take the same choice from the same sizes.
+    const int64_t P = (int64_t)a.T * a.topk;
+    const int64_t touched = P < a.E ? P : a.E;
+    const int maxb = P <= 48 * touched ? kPfMaxBlocksSmall : kPfMaxBlocks;
     if (stage == 1)
         hipLaunchKernelGGL(superblock_kernel, dim3(1), dim3(1024), 0, s, a.block_expert, (int)nblocks, a.E,
-                           list, count);
-    // Super-blocks: sum over experts of ceil(rows / 256) <= P / 256 + min(E, P) + 1.
-    const int64_t P = (int64_t)a.T * a.topk;
-    int64_t sbound = P / (kPfMaxBlocks * kPfBlockRows) + (P < a.E ? P : a.E) + 1;
+                           maxb, list, count);
+    // Super-blocks: sum over experts of ceil(rows / (32 maxb)) <= P / (32 maxb) + min(E, P) + 1.
+    int64_t sbound = P / (maxb * kPfBlockRows) + touched + 1;
     if (sbound > nblocks) sbound = nblocks;
     const int ntiles = stage == 1 ? a.I / 128 : a.H / 256;
     const int64_t grid = 8 * ((sbound + 7) / 8) * ntiles;
-    if (stage == 1)
-        hipLaunchKernelGGL(prefill_kernel<1>, dim3((unsigned)grid), dim3(kPfThreads), 0, s, a, list, count, ntiles);
-    else
-        hipLaunchKernelGGL(prefill_kernel<2>, dim3((unsigned)grid), dim3(kPfThreads), 0, s, a, list, count, ntiles);
+#define MOE_PF_LAUNCH(ST, NBM) \
+    hipLaunchKernelGGL((prefill_kernel<ST, NBM>), dim3((unsigned)grid), dim3(kPfThreads), 0, s, a, list, count, ntiles)
+    if (maxb == kPfMaxBlocksSmall) {
+        if (stage == 1) MOE_PF_LAUNCH(1, kPfMaxBlocksSmall);
+        else MOE_PF_LAUNCH(2, kPfMaxBlocksSmall);
+    } else {
+        if (stage == 1) MOE_PF_LAUNCH(1, kPfMaxBlocks);
+        else MOE_PF_LAUNCH(2, kPfMaxBlocks);
+    }
+#undef MOE_PF_LAUNCH
     return hipGetLastError();
 }
 

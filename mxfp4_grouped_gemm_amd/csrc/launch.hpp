@@ -56,7 +56,7 @@ hipError_t launch_gemv_stage(const MoeGemmArgs& a, int stage, hipStream_t s);
 // LDS-tiled MFMA kernels for prefill sizes (MXFP4, 32-row blocks, H and I
 // multiples of 256). Stage 1 first cuts the sorted blocks into super-blocks
 // (list in the workspace, prefill_list_bytes(cap) bytes); stage 2 reuses it.
-constexpr int64_t kPrefillMinPairs = 1024;
+constexpr int64_t kPrefillMinPairs = 32;
 bool prefill_eligible(const MoeGemmArgs& a);
 int64_t prefill_list_bytes(int64_t cap);
 hipError_t launch_prefill(const MoeGemmArgs& a, int stage, void* list_ws, hipStream_t s);
