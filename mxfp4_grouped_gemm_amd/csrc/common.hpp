@@ -76,6 +76,25 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, v);
 }
 
+// Eight two's-complement int4 codes (element e in nibble e, low nibble
+// first) times a bf16 group scale, split exactly into two bf16 vectors:
+// q * s is exact in fp32 but can need 11 significant bits; hi = bf16(q*s)
+// (RNE) and lo = q*s - hi (at most 3 significant bits, exact in bf16), so a
+// bf16 MFMA over hi and then lo sees the exact weight.
+__device__ __forceinline__ void int4x8_to_bf16_hilo(uint32_t d, float s, bf16x8& hi, bf16x8& lo) {
+    u32x4 h, l;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const float f0 = (float)((int)(d << (28 - 8 * k)) >> 28) * s;
+        const float f1 = (float)((int)(d << (24 - 8 * k)) >> 28) * s;
+        const uint32_t hp = pack_bf16x2(f0, f1);
+        h[k] = hp;
+        l[k] = pack_bf16x2(f0 - __uint_as_float(hp << 16), f1 - __uint_as_float(hp & 0xffff0000u));
+    }
+    hi = __builtin_bit_cast(bf16x8, h);
+    lo = __builtin_bit_cast(bf16x8, l);
+}
+
 __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }

@@ -30,6 +30,8 @@
 //    the main loop, so padding beyond the last 32-row block costs nothing.
 // Workgroups of one super-block sit on one XCD (consecutive workgroup ids go
 // round-robin over the 8 XCDs), so its activation rows stay in that L2.
+#include <type_traits>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -57,7 +59,7 @@ template <int NBMAX>
 struct __attribute__((aligned(16))) PfShared {
     uint8_t a[kPfABufs][NBMAX * kPfBlockRows * kPfRowBytes];
     uint8_t b[4][kPfWRows * 128];
-    uint8_t bs[4][kPfWRows * 8];
+    uint8_t bs[4][kPfWRows * 16];
     int32_t rows[NBMAX * kPfBlockRows];  // sorted_ids of the super-block
 };
 
@@ -133,7 +135,7 @@ __global__ __launch_bounds__(1024) void superblock_kernel(const int32_t* __restr
 //            -> h[sorted row] (bf16).
 //   STAGE 2: A = h rows (contiguous), K = I; wave w owns columns
 //            n0+64w.. +64 of w2; epilogue y[pair] (fp32).
-template <int STAGE, int NB, int NBMAX>
+template <int STAGE, int FMT, int NB, int NBMAX>
 __device__ __forceinline__ void pf_tile(const MoeGemmArgs& a, PfShared<NBMAX>& sh, int e, int row0, int n0) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -141,6 +143,7 @@ __device__ __forceinline__ void pf_tile(const MoeGemmArgs& a, PfShared<NBMAX>& s
     const int P = a.T * a.topk;
     const int K = STAGE == 1 ? a.H : a.I;
     const int nchunks = K / kPfChunk;
+    constexpr int SB = FMT == kFmtMxfp4 ? 1 : 2;  // bytes per group scale
 
     // --- activations: thread t moves row 32i + t/8, logical piece t%8 of
     // every 32-row block i; in LDS the piece sits at t%8 ^ ((row/2) % 8).
@@ -176,10 +179,10 @@ __device__ __forceinline__ void pf_tile(const MoeGemmArgs& a, PfShared<NBMAX>& s
     if (STAGE == 1) {
         const int64_t slab = 2 * (int64_t)a.I;
         rw = make_rsrc(a.w13 + (int64_t)e * slab * (a.H / 2), (uint32_t)(slab * (a.H / 2)));
-        rs = make_rsrc((const uint8_t*)a.w13_scale + (int64_t)e * slab * (a.H / 32), (uint32_t)(slab * (a.H / 32)));
+        rs = make_rsrc((const uint8_t*)a.w13_scale + (int64_t)e * slab * (a.H / 32) * SB, (uint32_t)(slab * (a.H / 32) * SB));
     } else {
         rw = make_rsrc(a.w2 + (int64_t)e * a.H * (a.I / 2), (uint32_t)((int64_t)a.H * (a.I / 2)));
-        rs = make_rsrc((const uint8_t*)a.w2_scale + (int64_t)e * a.H * (a.I / 32), (uint32_t)((int64_t)a.H * (a.I / 32)));
+        rs = make_rsrc((const uint8_t*)a.w2_scale + (int64_t)e * a.H * (a.I / 32) * SB, (uint32_t)((int64_t)a.H * (a.I / 32) * SB));
     }
     // Stage loads: instruction j moves rows 8j..8j+7, eight lanes (128
     // contiguous bytes, one cache line) per row; the scale bytes of row
@@ -187,25 +190,35 @@ __device__ __forceinline__ void pf_tile(const MoeGemmArgs& a, PfShared<NBMAX>& s
     uint32_t boff[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) boff[j] = grow(8 * j + (lane >> 3)) * (uint32_t)(K / 2) + 16u * (lane & 7);
-    const uint32_t soff = grow(lane) * (uint32_t)(K / 32);
+    const uint32_t soff = grow(lane) * (uint32_t)(K / 32 * SB);
     const int nstages = nchunks / kPfStage;
-    u32x4 braw[8];
-    u32x2 sraw;
-    auto issue_bstage = [&](int st) {
+    // Register slots for weight stages in flight: two when the tile is
+    // small (memory-bound decode batches: a stage round trip per four
+    // chunks would bound the stream), else one.
+    constexpr int BR = 1;
+    u32x4 braw[BR][8];
+    // the stage's 8 group scales of row `lane`: 8 e8m0 bytes or 8 bf16
+    using svec = typename std::conditional<FMT == kFmtMxfp4, u32x2, u32x4>::type;
+    constexpr int SVB = (int)sizeof(svec);
+    svec sraw[BR];
+    auto issue_bstage = [&](int slot, int st) {
         const bool ok = st < nstages;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) braw[j] = bld16(rw, ok ? boff[j] + 128u * st : kOob);
-        sraw = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, ok ? soff + 8u * st : kOob, 0, 0));
+        for (int j = 0; j < 8; ++j) braw[slot][j] = bld16(rw, ok ? boff[j] + 128u * st : kOob);
+        if constexpr (FMT == kFmtMxfp4)
+            sraw[slot] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, ok ? soff + 8u * st : kOob, 0, 0));
+        else
+            sraw[slot] = bld16(rs, ok ? soff + 16u * st : kOob);
     };
     uint8_t* const wl = sh.b[w];
     uint8_t* const sl = sh.bs[w];
-    auto store_bstage = [&]() {
+    auto store_bstage = [&](int slot) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const int r = 8 * j + (lane >> 3);
-            *(u32x4*)(wl + r * 128 + (((lane & 7) ^ ((r >> 1) & 7)) << 4)) = braw[j];
+            *(u32x4*)(wl + r * 128 + (((lane & 7) ^ ((r >> 1) & 7)) << 4)) = braw[slot][j];
         }
-        *(u32x2*)(sl + lane * 8) = sraw;
+        *(svec*)(sl + lane * SVB) = sraw[slot];
     };
     // MFMA B operand of chunk j of the stage, block nb: row 32nb + nl,
     // logical piece 2j + half (16 bytes = one MX block of 32 codes).
@@ -216,14 +229,30 @@ __device__ __forceinline__ void pf_tile(const MoeGemmArgs& a, PfShared<NBMAX>& s
             dst[nb] = *(const u32x4*)(wl + r * 128 + (((2 * j + half) ^ ((r >> 1) & 7)) << 4));
         }
     };
-    auto read_scales = [&](u32x2 (&dst)[2]) {
+    auto read_scales = [&](svec (&dst)[2]) {
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) dst[nb] = *(const u32x2*)(sl + (32 * nb + nl) * 8);
+        for (int nb = 0; nb < 2; ++nb) dst[nb] = *(const svec*)(sl + (32 * nb + nl) * SVB);
     };
-    // e8m0 byte of chunk j (block 2j + half of the stage) as a scale operand.
-    auto scale_of = [&](const u32x2& w8, int j) -> float {
-        const uint32_t word = j < 2 ? w8[0] : w8[1];
-        return e8m0_scale_operand((word >> (16 * (j & 1) + 8 * half)) & 0xffu);
+    // Scale of chunk j (group 2j + half of the stage): the e8m0 byte as the
+    // fp4 converts' scale operand, or the bf16 int4 group scale as a float.
+    auto scale_of = [&](const svec& w8, int j) -> float {
+        if constexpr (FMT == kFmtMxfp4) {
+            const uint32_t word = j < 2 ? w8[0] : w8[1];
+            return e8m0_scale_operand((word >> (16 * (j & 1) + 8 * half)) & 0xffu);
+        } else {
+            return __uint_as_float(((w8[j] >> (16 * half)) & 0xffffu) << 16);
+        }
+    };
+    // Decoded weight operand of one k-step: MXFP4 is exact in bf16; int4 is
+    // an exact hi + lo pair (two MFMAs).
+    struct Bop {
+        bf16x8 hi, lo;
+    };
+    auto decode = [&](uint32_t d, float sc) -> Bop {
+        Bop r;
+        if constexpr (FMT == kFmtMxfp4) r.hi = mxfp4x8_to_bf16(d, sc);
+        else int4x8_to_bf16_hilo(d, sc, r.hi, r.lo);
+        return r;
     };
 
     // Activation ring: chunk k lives in slot k % DA from its load (DA chunks
@@ -231,7 +260,7 @@ __device__ __forceinline__ void pf_tile(const MoeGemmArgs& a, PfShared<NBMAX>& s
     // in order, so this depth is the latency budget of every load; it is as
     // deep as the registers allow. Chunks past the end are issued with
     // out-of-range offsets (zeros, no traffic).
-    constexpr int DA = NB <= 6 ? 4 : 2;
+    constexpr int DA = (NB >= 3 && NB <= 6 && FMT == kFmtMxfp4) ? 4 : 2;
     u32x4 ar[DA][NB];
     auto issue_a = [&](int slot, int c) {
         const bool ok = c < nchunks;
@@ -270,29 +299,48 @@ __device__ __forceinline__ void pf_tile(const MoeGemmArgs& a, PfShared<NBMAX>& s
     // read one chunk ahead); stage t+1 is then loaded into the registers.
     issue_a(0, 0);
     issue_a(1, 1);
-    issue_bstage(0);
+    issue_bstage(0, 0);
     store_a(0, 0);
     store_a(1, 1);
-    store_bstage();
-    issue_bstage(1);
+    store_bstage(0);
+#pragma unroll
+    for (int t = 1; t <= BR; ++t) issue_bstage(t % BR, t);
 #pragma unroll
     for (int k = 2; k < 2 + DA; ++k) issue_a(k % DA, k);
     __syncthreads();
-    read_a(0, 0, 0);
+    // Small tiles (1-2 blocks) have too few MFMAs per k-step to cover an LDS
+    // read between consecutive steps: they read a whole chunk's operands one
+    // chunk ahead instead.
+    constexpr bool CP = NB <= 2 && FMT == kFmtMxfp4;
+    bf16x8 avc[4][NB], avn[4][NB];
+    auto read_a_chunk = [&](bf16x8 (&dst)[4][NB], int buf) {
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) {
+            const uint8_t* base = sh.a[buf] + nl * kPfRowBytes + (((4 * half + s4) ^ sw) << 4);
+#pragma unroll
+            for (int i = 0; i < NB; ++i) dst[s4][i] = *(const bf16x8*)(base + 32 * i * kPfRowBytes);
+        }
+    };
+    if (CP) read_a_chunk(avc, 0);
+    else read_a(0, 0, 0);
     u32x4 bcur[2], bnext[2];
-    u32x2 scur[2], snext[2];
+    svec scur[2], snext[2];
     read_scales(scur);
     read_bchunk(bcur, 0);
     // Decoded weights of the current k-step; the next step's are decoded
     // while this step's MFMAs run.
-    bf16x8 b0 = mxfp4x8_to_bf16(bcur[0][0], scale_of(scur[0], 0));
-    bf16x8 b1 = mxfp4x8_to_bf16(bcur[1][0], scale_of(scur[1], 0));
+    Bop b0 = decode(bcur[0][0], scale_of(scur[0], 0));
+    Bop b1 = decode(bcur[1][0], scale_of(scur[1], 0));
 
     int buf = 0;  // chunk c's LDS buffer, c % 3
-    for (int c0 = 0; c0 < nchunks; c0 += kPfStage) {
+    // Unrolled over BR stages so every register slot index is a constant;
+    // u4 = chunk within its stage.
+    for (int c0 = 0; c0 < nchunks; c0 += kPfStage * BR) {
 #pragma unroll
-        for (int u = 0; u < kPfStage; ++u) {
-            const int c = c0 + u;
+        for (int uu = 0; uu < kPfStage * BR; ++uu) {
+            const int u = uu & 3;
+            const int tslot = uu >> 2;  // this stage's index modulo BR
+            const int c = c0 + uu;
             const int buf1 = buf == 2 ? 0 : buf + 1;
             const int buf2 = buf1 == 2 ? 0 : buf1 + 1;
             const float sc0 = scale_of(scur[0], u);
@@ -309,27 +357,34 @@ __device__ __forceinline__ void pf_tile(const MoeGemmArgs& a, PfShared<NBMAX>& s
                     }
                     store_a((u + 2) % DA, buf2);  // A(c+2)
                     issue_a((u + 2) % DA, c + 2 + DA);
-                    if (u == 2) {  // stage c0/4 + 1 into LDS, load the one after
-                        store_bstage();
-                        issue_bstage(c0 / kPfStage + 2);
+                    if (u == 2) {  // next stage into LDS, its slot reloaded BR stages ahead
+                        const int slot = (tslot + 1) % BR;
+                        store_bstage(slot);
+                        issue_bstage(slot, (c0 + 4 * tslot) / kPfStage + 1 + BR);
                     }
+                    if (CP) read_a_chunk(avn, buf1);
                 }
                 // Operands of the next k-step (the next chunk's first at s = 3).
-                bf16x8 n0, n1;
+                Bop n0, n1;
                 if (s < 3) {
-                    read_a((s + 1) & 1, buf, s + 1);
-                    n0 = mxfp4x8_to_bf16(bcur[0][s + 1], sc0);
-                    n1 = mxfp4x8_to_bf16(bcur[1][s + 1], sc1);
+                    if (!CP) read_a((s + 1) & 1, buf, s + 1);
+                    n0 = decode(bcur[0][s + 1], sc0);
+                    n1 = decode(bcur[1][s + 1], sc1);
                 } else {
-                    read_a(0, buf1, 0);
-                    const u32x2* sn = u < 3 ? scur : snext;
-                    n0 = mxfp4x8_to_bf16(bnext[0][0], scale_of(sn[0], (u + 1) & 3));
-                    n1 = mxfp4x8_to_bf16(bnext[1][0], scale_of(sn[1], (u + 1) & 3));
+                    if (!CP) read_a(0, buf1, 0);
+                    const svec* sn = u < 3 ? scur : snext;
+                    n0 = decode(bnext[0][0], scale_of(sn[0], (u + 1) & 3));
+                    n1 = decode(bnext[1][0], scale_of(sn[1], (u + 1) & 3));
                 }
 #pragma unroll
                 for (int i = 0; i < NB; ++i) {
-                    acc[i][0] = mfma32(av[s & 1][i], b0, acc[i][0]);
-                    acc[i][1] = mfma32(av[s & 1][i], b1, acc[i][1]);
+                    const bf16x8 ai = CP ? avc[s][i] : av[s & 1][i];
+                    acc[i][0] = mfma32(ai, b0.hi, acc[i][0]);
+                    acc[i][1] = mfma32(ai, b1.hi, acc[i][1]);
+                    if constexpr (FMT != kFmtMxfp4) {
+                        acc[i][0] = mfma32(ai, b0.lo, acc[i][0]);
+                        acc[i][1] = mfma32(ai, b1.lo, acc[i][1]);
+                    }
                 }
                 // Interleave: each MFMA pair is followed by an operand read
                 // and a couple of converts for the next step (and at s = 0 by
@@ -355,7 +410,19 @@ __device__ __forceinline__ void pf_tile(const MoeGemmArgs& a, PfShared<NBMAX>& s
                 scur[0] = snext[0];
                 scur[1] = snext[1];
             }
-            __syncthreads();  // A(c+2) visible; buffer c%3 free for A(c+3)
+            if (CP) {
+#pragma unroll
+                for (int s4 = 0; s4 < 4; ++s4)
+#pragma unroll
+                    for (int i = 0; i < NB; ++i) avc[s4][i] = avn[s4][i];
+            }
+            // Barrier: A(c+2) visible, buffer c%3 free for A(c+3). Only the
+            // LDS operations older than the last NB (the next chunk's first
+            // operand reads, issued in the k-step just before) must be
+            // complete; those reads stay in flight across the barrier.
+            // (With chunk-level reads every LDS operation completes first.)
+            if (CP) __syncthreads();
+            else asm volatile("s_waitcnt lgkmcnt(%0)\n\ts_barrier" ::"n"(NB) : "memory");
             buf = buf1;
         }
     }
@@ -394,7 +461,7 @@ __device__ __forceinline__ void pf_tile(const MoeGemmArgs& a, PfShared<NBMAX>& s
     }
 }
 
-template <int STAGE, int NBMAX>
+template <int STAGE, int FMT, int NBMAX>
 __global__ __launch_bounds__(kPfThreads, NBMAX <= 2 ? 2 : 1) void prefill_kernel(MoeGemmArgs a,
                                                                                const int4* __restrict__ list,
                                                                                const int* __restrict__ count,
@@ -414,24 +481,25 @@ __global__ __launch_bounds__(kPfThreads, NBMAX <= 2 ? 2 : 1) void prefill_kernel
     __syncthreads();
     const int n0 = nt * (STAGE == 1 ? 128 : 256);
     if constexpr (NBMAX <= 2) {
-        if (nb == 1) pf_tile<STAGE, 1>(a, sh, e, row0, n0);
-        else pf_tile<STAGE, 2>(a, sh, e, row0, n0);
+        if (nb == 1) pf_tile<STAGE, FMT, 1>(a, sh, e, row0, n0);
+        else pf_tile<STAGE, FMT, 2>(a, sh, e, row0, n0);
     } else {
         switch (nb) {
-            case 1: pf_tile<STAGE, 1>(a, sh, e, row0, n0); break;
-            case 2: pf_tile<STAGE, 2>(a, sh, e, row0, n0); break;
-            case 3: pf_tile<STAGE, 3>(a, sh, e, row0, n0); break;
-            case 4: pf_tile<STAGE, 4>(a, sh, e, row0, n0); break;
-            case 5: pf_tile<STAGE, 5>(a, sh, e, row0, n0); break;
-            case 6: pf_tile<STAGE, 6>(a, sh, e, row0, n0); break;
-            case 7: pf_tile<STAGE, 7>(a, sh, e, row0, n0); break;
-            default: pf_tile<STAGE, 8>(a, sh, e, row0, n0); break;
+            case 1: pf_tile<STAGE, FMT, 1>(a, sh, e, row0, n0); break;
+            case 2: pf_tile<STAGE, FMT, 2>(a, sh, e, row0, n0); break;
+            case 3: pf_tile<STAGE, FMT, 3>(a, sh, e, row0, n0); break;
+            case 4: pf_tile<STAGE, FMT, 4>(a, sh, e, row0, n0); break;
+            case 5: pf_tile<STAGE, FMT, 5>(a, sh, e, row0, n0); break;
+            case 6: pf_tile<STAGE, FMT, 6>(a, sh, e, row0, n0); break;
+            case 7: pf_tile<STAGE, FMT, 7>(a, sh, e, row0, n0); break;
+            default: pf_tile<STAGE, FMT, 8>(a, sh, e, row0, n0); break;
         }
     }
 }
 
 bool prefill_eligible(const MoeGemmArgs& a) {
-    return a.fmt == kFmtMxfp4 && a.bm == kPfBlockRows && a.H % 256 == 0 && a.I % 256 == 0 &&
+    return (a.fmt == kFmtMxfp4 || a.fmt == kFmtInt4g32) && a.bm == kPfBlockRows && a.H % 256 == 0 &&
+           a.I % 256 == 0 && (int64_t)2 * a.I * (a.H / 32) * 2 < 0x7fff0000LL &&
            (int64_t)a.T * a.topk * a.H * 4 < 0x7fff0000LL &&
            a.cap * a.I * 2 < 0x7fff0000LL && (int64_t)a.T * a.H * 2 < 0x7fff0000LL &&
            (int64_t)2 * a.I * (a.H / 2) < 0x7fff0000LL;
@@ -457,15 +525,21 @@ hipError_t launch_prefill(const MoeGemmArgs& a, int stage, void* list_ws, hipStr
     if (sbound > nblocks) sbound = nblocks;
     const int ntiles = stage == 1 ? a.I / 128 : a.H / 256;
     const int64_t grid = 8 * ((sbound + 7) / 8) * ntiles;
-#define MOE_PF_LAUNCH(ST, NBM) \
-    hipLaunchKernelGGL((prefill_kernel<ST, NBM>), dim3((unsigned)grid), dim3(kPfThreads), 0, s, a, list, count, ntiles)
+#define MOE_PF_LAUNCH(ST, F, NBM) \
+    hipLaunchKernelGGL((prefill_kernel<ST, F, NBM>), dim3((unsigned)grid), dim3(kPfThreads), 0, s, a, list, count, ntiles)
+#define MOE_PF_LAUNCH_F(ST, NBM)                                   \
+    do {                                                           \
+        if (a.fmt == kFmtMxfp4) MOE_PF_LAUNCH(ST, kFmtMxfp4, NBM); \
+        else MOE_PF_LAUNCH(ST, kFmtInt4g32, NBM);                 \
+    } while (0)
     if (maxb == kPfMaxBlocksSmall) {
-        if (stage == 1) MOE_PF_LAUNCH(1, kPfMaxBlocksSmall);
-        else MOE_PF_LAUNCH(2, kPfMaxBlocksSmall);
+        if (stage == 1) MOE_PF_LAUNCH_F(1, kPfMaxBlocksSmall);
+        else MOE_PF_LAUNCH_F(2, kPfMaxBlocksSmall);
     } else {
-        if (stage == 1) MOE_PF_LAUNCH(1, kPfMaxBlocks);
-        else MOE_PF_LAUNCH(2, kPfMaxBlocks);
+        if (stage == 1) MOE_PF_LAUNCH_F(1, kPfMaxBlocks);
+        else MOE_PF_LAUNCH_F(2, kPfMaxBlocks);
     }
+#undef MOE_PF_LAUNCH_F
 #undef MOE_PF_LAUNCH
     return hipGetLastError();
 }

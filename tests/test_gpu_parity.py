@@ -255,6 +255,22 @@ def test_forward_prefill_path(moe, T, H, I, E, topk, hot):
           f"max|ref| {np.abs(ref).max() / rms:.1f} RMS")
 
 
+def test_int4_forward_prefill_path(moe):
+    """int4-g32 weights on the LDS-tiled MFMA kernels: requantize on the GPU
+    (bit-exact against the oracle elsewhere), then compare the whole layer
+    with the oracle's int4 forward on the oracle's own requantized weights."""
+    T, H, I, E, topk = 96, 512, 256, 8, 4
+    wl = synth.small(T=T, H=H, I=I, E=E, topk=topk, seed=77)
+    q13, s13 = moe.requantize_mxfp4_experts(dev(wl.w13), dev(wl.w13_scale))
+    q2, s2 = moe.requantize_mxfp4_experts(dev(wl.w2), dev(wl.w2_scale))
+    out = run_layer(moe, wl, topk, fmt=1, w=(q13, s13, q2, s2))
+    rq13, rs13 = oracle.requant_int4g32(wl.w13, wl.w13_scale)
+    rq2, rs2 = oracle.requant_int4g32(wl.w2, wl.w2_scale)
+    ids, w = oracle.route_topk(wl.logits, topk)
+    ref = oracle.moe_forward(wl.x, rq13, rs13, rq2, rs2, 1, ids, w, I=I)
+    check_close_bf16_out(out_f64(out), ref, "int4 prefill path")
+
+
 def test_forward_precomputed_routing_matches_oracle_inputs(moe):
     """apply()-style call: routing from the oracle fed to the GPU forward."""
     wl = synth.small(T=9, H=256, I=128, E=8, topk=3, seed=31)
