@@ -13,7 +13,9 @@
 //
 // route_align_kernel runs the routing of up to 64 tokens (route.hpp, one
 // wave per token) in the same workgroup and sorts straight from LDS, saving
-// a launch and a round trip of the ids through memory at decode sizes.
+// a launch and a round trip of the ids through memory at decode sizes;
+// route_align_small_kernel does the same for up to 64 pairs with a one-wave
+// sort.
 #include "common.hpp"
 #include "launch.hpp"
 #include "route.hpp"
@@ -136,6 +138,69 @@ __global__ __launch_bounds__(kSortThreads) void route_align_kernel(
                     num_post_pad);
 }
 
+// Up to 64 pairs: route with up to four waves, then one wave sorts with
+// one pair per lane and no workgroup barrier after the routing. A pair's
+// position is (padded start of its expert) + (pairs of the same expert
+// before it), both counted over the wave with readlane loops; the padded
+// start of an expert sums the padded lengths of the smaller experts present.
+// Same outputs as align_sort_body.
+constexpr int kSmallPairs = 64;
+constexpr int kSmallPairsFused = 16;  // measured: above this the 1024-thread sort is faster
+
+template <int VPL>
+__global__ __launch_bounds__(256) void route_align_small_kernel(
+    const float* __restrict__ logits, int T, int E, int topk, int renorm, int bm, int64_t cap,
+    int32_t* __restrict__ ids, float* __restrict__ weights, int32_t* __restrict__ sorted_ids,
+    int32_t* __restrict__ block_expert, int32_t* __restrict__ expert_offsets,
+    int32_t* __restrict__ num_post_pad) {
+    __shared__ int32_t ids_lds[kSmallPairs];
+    const int wv = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    for (int t = wv; t < T; t += 4)
+        route_token<VPL>(logits + (int64_t)t * E, E, topk, renorm, ids + (int64_t)t * topk,
+                         weights + (int64_t)t * topk, ids_lds + t * topk);
+    __syncthreads();
+    if (wv != 0) return;
+    const int P = T * topk;
+    const int e = lane < P ? ids_lds[lane] : -1;
+    const bool valid = (unsigned)e < (unsigned)E;
+    int cnt = 0, before = 0;
+    for (int q = 0; q < P; ++q) {
+        const int eq = __builtin_amdgcn_readlane(e, q);
+        const bool same = valid && eq == e;
+        cnt += same ? 1 : 0;
+        before += (same && q < lane) ? 1 : 0;
+    }
+    const bool leader = valid && before == 0;
+    const int padded = (cnt + bm - 1) / bm * bm;
+    const uint64_t leaders = __ballot(leader);
+    // Padded start of this lane's expert, and the total.
+    int start = 0, total = 0;
+    for (uint64_t m = leaders; m; m &= m - 1ull) {
+        const int q = __ffsll((unsigned long long)m) - 1;
+        const int eq = __builtin_amdgcn_readlane(e, q);
+        const int pq = __builtin_amdgcn_readlane(padded, q);
+        start += (valid && eq < e) ? pq : 0;
+        total += pq;
+    }
+    if (valid) sorted_ids[start + before] = lane;
+    if (leader) {
+        for (int r = start + cnt; r < start + padded; ++r) sorted_ids[r] = P;
+        for (int b = start / bm; b < (start + padded) / bm; ++b) block_expert[b] = e;
+    }
+    for (int64_t r = total + lane; r < cap; r += 64) sorted_ids[r] = P;
+    for (int64_t b = total / bm + lane; b < cap / bm; b += 64) block_expert[b] = -1;
+    for (int x = lane; x <= E; x += 64) {
+        int off = 0;
+        for (uint64_t m = leaders; m; m &= m - 1ull) {
+            const int q = __ffsll((unsigned long long)m) - 1;
+            off += __builtin_amdgcn_readlane(e, q) < x ? __builtin_amdgcn_readlane(padded, q) : 0;
+        }
+        expert_offsets[x] = off;
+    }
+    if (lane == 0) num_post_pad[0] = total;
+}
+
 hipError_t launch_align_sort(const int32_t* ids, int P, int E, int bm, int64_t cap,
                              int32_t* sorted_ids, int32_t* block_expert, int32_t* expert_offsets,
                              int32_t* num_post_pad, hipStream_t s) {
@@ -154,9 +219,16 @@ hipError_t launch_route_align(const float* logits, int T, int E, int topk, int r
                               hipStream_t s) {
     const dim3 grid(1), block(kSortThreads);
     const int vpl = (E + 63) / 64;
-#define MOE_LAUNCH_RA(V)                                                                          \
-    hipLaunchKernelGGL(route_align_kernel<V>, grid, block, 0, s, logits, T, E, topk, renorm, bm, \
-                       cap, ids, weights, sorted_ids, block_expert, expert_offsets, num_post_pad)
+#define MOE_LAUNCH_RA(V)                                                                                 \
+    do {                                                                                                 \
+        if ((int64_t)T * topk <= kSmallPairsFused)                                                       \
+            hipLaunchKernelGGL(route_align_small_kernel<V>, dim3(1), dim3(256), 0, s, logits, T, E, topk, \
+                               renorm, bm, cap, ids, weights, sorted_ids, block_expert, expert_offsets,  \
+                               num_post_pad);                                                            \
+        else                                                                                             \
+            hipLaunchKernelGGL(route_align_kernel<V>, grid, block, 0, s, logits, T, E, topk, renorm, bm, \
+                               cap, ids, weights, sorted_ids, block_expert, expert_offsets, num_post_pad); \
+    } while (0)
     if (vpl <= 1) MOE_LAUNCH_RA(1);
     else if (vpl <= 2) MOE_LAUNCH_RA(2);
     else if (vpl <= 4) MOE_LAUNCH_RA(4);

@@ -154,8 +154,11 @@ __device__ __forceinline__ void gemv_dot(const GemvWeights<NCH>& W, const uint8_
 }
 
 // Stage 1: unit = (expert block b, columns i0, i0+1 of I): gate rows i0,
-// i0+1 and up rows I+i0, I+i0+1, against the block's <= NR token rows.
-template <int NR, int NCH>
+// i0+1 and up rows I+i0, I+i0+1, against the block's <= NRMAX token rows.
+// The activations of the first NR rows are loaded with the weights; further
+// rows (rare at decode sizes) reuse those registers one row at a time, so
+// the register footprint -- and the occupancy -- is that of NR rows.
+template <int NR, int NRMAX, int NCH>
 __global__ __launch_bounds__(kGemvWaves1 * 64) void stage1_gemv_kernel(MoeGemmArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t lds_scale[kGemvWaves1][4 * 64 * NCH];
     const int lane = threadIdx.x & 63;
@@ -168,9 +171,9 @@ __global__ __launch_bounds__(kGemvWaves1 * 64) void stage1_gemv_kernel(MoeGemmAr
     const int64_t row0 = b * a.bm;
     const int e = a.block_expert[b];
     const int P = a.T * a.topk;
-    int pair[NR], nvalid = 0;
+    int pair[NRMAX], nvalid = 0;
 #pragma unroll
-    for (int m = 0; m < NR; ++m) {
+    for (int m = 0; m < NRMAX; ++m) {
         pair[m] = a.sorted_ids[row0 + m];
         nvalid += (pair[m] >= 0 && pair[m] < P) ? 1 : 0;
     }
@@ -182,22 +185,25 @@ __global__ __launch_bounds__(kGemvWaves1 * 64) void stage1_gemv_kernel(MoeGemmAr
     const rsrc_t rw = make_rsrc(a.w13 + e * slab_rows * (H / 2), (uint32_t)(slab_rows * (H / 2)));
     const rsrc_t rs = make_rsrc((const uint8_t*)a.w13_scale + e * slab_rows * nblk, (uint32_t)(slab_rows * nblk));
     const rsrc_t rx = make_rsrc(a.x, (uint32_t)((int64_t)a.T * H * 2));
+    auto x_off = [&](int m) -> uint32_t {
+        return m < nvalid ? (uint32_t)(pair[m] / a.topk) * (uint32_t)(2 * H) : kOob;
+    };
     // Activations first: the oldest loads, so waiting for them never waits
     // for the weight stream issued after them.
     u32x4 x[NR][NCH][4];
 #pragma unroll
-    for (int m = 0; m < NR; ++m)
-        issue_x<NCH>(x[m], rx, m < nvalid ? (uint32_t)(pair[m] / a.topk) * (uint32_t)(2 * H) : kOob, nblk, lane);
+    for (int m = 0; m < NR; ++m) issue_x<NCH>(x[m], rx, x_off(m), nblk, lane);
     GemvWeights<NCH> W;
     W.issue(rw, rs, GemvRows{i0, 2, I + i0}, nblk, lane);
     W.stage_scales(lds_scale[wave], nblk, lane);
     wave_lds_sync();
 
 #pragma unroll
-    for (int m = 0; m < NR; ++m) {
+    for (int m = 0; m < NRMAX; ++m) {
         if (m >= nvalid) break;
+        if (m >= NR) issue_x<NCH>(x[m % NR], rx, x_off(m), nblk, lane);
         float acc[4] = {0.f, 0.f, 0.f, 0.f};
-        gemv_dot<NCH>(W, lds_scale[wave], x[m], nblk, lane, acc);
+        gemv_dot<NCH>(W, lds_scale[wave], x[m % NR], nblk, lane, acc);
         // acc: gate i0, gate i0+1, up i0, up i0+1. With v = (g0, u0, g1, u1)
         // the rows after reduce4 hold (g0, g1, u0, u1); a permlane32 swap of
         // the sum with itself puts (g0, u0) in lanes 0..15, (g1, u1) in 16..31.
@@ -284,12 +290,12 @@ bool gemv_eligible(const MoeGemmArgs& a) {
            (int64_t)a.T * a.topk * a.I * 2 < 0x7fff0000LL;
 }
 
-template <int NR>
+template <int NRMAX>
 static void launch_stage1_nr(const MoeGemmArgs& a, int nch, hipStream_t s) {
     const int64_t units = (a.cap / a.bm) * (a.I / 2);
     const dim3 grid((unsigned)((units + kGemvWaves1 - 1) / kGemvWaves1)), block(kGemvWaves1 * 64);
-    if (nch == 1) hipLaunchKernelGGL((stage1_gemv_kernel<NR, 1>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((stage1_gemv_kernel<NR, 2>), grid, block, 0, s, a);
+    if (nch == 1) hipLaunchKernelGGL((stage1_gemv_kernel<1, NRMAX, 1>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((stage1_gemv_kernel<1, NRMAX, 2>), grid, block, 0, s, a);
 }
 
 hipError_t launch_gemv_stage(const MoeGemmArgs& a, int stage, hipStream_t s) {
