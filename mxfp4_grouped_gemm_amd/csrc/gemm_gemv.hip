@@ -16,11 +16,11 @@
 //    sums meet with permlane32/16 swaps and DPP row rotations.
 //
 // Stage 1 is block-major (one expert block, its <= 4 rows share the weight
-// stream) and stores h by pair index. Stage 2 is token-major: a 512-thread
-// workgroup owns (token, 4 output columns), its 8 waves take the token's
-// top-k slots (expert of slot j from topk_ids), scale each slot's partial
-// sums by the router weight and meet in LDS in a fixed order, so the weighted
-// combine happens in the same launch and no per-pair output is stored.
+// stream) and stores h by pair index. Stage 2 is token-major: a workgroup
+// owns (token, a run of output rows) with one wave per top-k slot (expert of
+// slot j from topk_ids); each wave scales its row sums by the router weight
+// and the slots meet in LDS in a fixed order, so the weighted combine
+// happens in the same launch and no per-pair output is stored.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -283,6 +283,140 @@ __global__ __launch_bounds__(kGemvWaves2 * 64) void stage2_gemv_tok_kernel(MoeGe
     }
 }
 
+// Stage 2 + combine, persistent over a run of output rows: workgroup =
+// (token t, rows [row0, row0 + nrows)), one wave per top-k slot j. The wave
+// keeps its pair's h row in registers for the whole run and streams its
+// expert's down rows four at a time, the next four in flight while the
+// current ones are dotted, so every CU keeps a steady stream of weight loads
+// in flight instead of draining between short workgroups. Router-weighted
+// row sums go to LDS; after one barrier the rows are summed over the slots
+// in ascending j, the combine's order.
+constexpr int kRowsMax = 64;   // rows per workgroup (bounds the LDS sums)
+constexpr int kSlotsMax = 16;  // waves per workgroup = top-k
+
+// Four weight rows in half-block units: lane l holds half-block 64c + l
+// (16 K elements, 8 code bytes) of each row, so K = 16 * nhb fills the lanes
+// evenly whenever nhb is a multiple of 64 (I = 3072: three chunks, no idle
+// lane). Rows first .. first + nv - 1 (nv <= 4) of one expert; further row
+// slots load nothing.
+template <int NHC>
+struct HalfRows {
+    u32x2 w[4][NHC];
+    u32x4 sc;  // this lane's 16-byte piece of the rows' scale bytes
+
+    __device__ __forceinline__ void issue_run(rsrc_t rw, rsrc_t rs, int first, int nv, int nhb, int lane) {
+        const int nblk = nhb / 2, ptot = nv * nblk / 16;
+        sc = bld16(rs, lane < ptot ? (uint32_t)first * nblk + 16u * lane : kOob);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int c = 0; c < NHC; ++c) {
+                const int hb = 64 * c + lane;
+                w[r][c] = bld8(rw, (r < nv && hb < nhb) ? (uint32_t)(first + r) * (uint32_t)(nhb * 8) + 8u * hb
+                                                        : kOob);
+            }
+    }
+    __device__ __forceinline__ void stage_scales(uint8_t* lds, int nhb, int lane) const {
+        if (lane < 4 * (nhb / 2) / 16) *(u32x4*)(lds + 16 * lane) = sc;
+    }
+};
+
+template <int NHC>
+__device__ __forceinline__ void issue_xh(u32x4 (&x)[NHC][2], rsrc_t rx, uint32_t x_off, int nhb, int lane) {
+#pragma unroll
+    for (int c = 0; c < NHC; ++c) {
+        const int hb = 64 * c + lane;
+        const uint32_t o = (x_off != kOob && hb < nhb) ? x_off + 32u * hb : kOob;
+        x[c][0] = bld16(rx, o);
+        x[c][1] = bld16(rx, o + 16u);
+    }
+}
+
+template <int NHC>
+__device__ __forceinline__ void half_dot(const HalfRows<NHC>& W, const uint8_t* lds_scale,
+                                         const u32x4 (&x)[NHC][2], int nhb, int lane, float (&acc)[4]) {
+    const int nblk = nhb / 2;
+#pragma unroll
+    for (int c = 0; c < NHC; ++c) {
+        const int hb = 64 * c + lane;
+        const int sblk = (hb < nhb ? hb : nhb - 1) >> 1;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float sc = e8m0_scale_operand(lds_scale[r * nblk + sblk]);
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const bf16x8 wv = mxfp4x8_to_bf16(W.w[r][c][q], sc);
+                const bf16x8 xv = __builtin_bit_cast(bf16x8, x[c][q]);
+                acc[r] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(wv, wv, 0, 1),
+                                                         __builtin_shufflevector(xv, xv, 0, 1), acc[r], false);
+                acc[r] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(wv, wv, 2, 3),
+                                                         __builtin_shufflevector(xv, xv, 2, 3), acc[r], false);
+                acc[r] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(wv, wv, 4, 5),
+                                                         __builtin_shufflevector(xv, xv, 4, 5), acc[r], false);
+                acc[r] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_shufflevector(wv, wv, 6, 7),
+                                                         __builtin_shufflevector(xv, xv, 6, 7), acc[r], false);
+            }
+        }
+    }
+}
+
+template <int NHC>
+__global__ __launch_bounds__(kSlotsMax * 64) void stage2_gemv_rows_kernel(MoeGemmArgs a, int G, int R) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds_scale[kSlotsMax][2][4 * 32 * NHC];
+    __shared__ float red[kSlotsMax][kRowsMax];
+    const int lane = threadIdx.x & 63;
+    const int j = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    // Workgroups of one row run (all tokens) are consecutive in L and land
+    // on one XCD, so tokens routed to the same expert share its rows in L2.
+    const int nbp = (int)gridDim.x;  // a multiple of 8
+    const int L = (int)(blockIdx.x % 8) * (nbp / 8) + (int)(blockIdx.x / 8);
+    if (L >= a.T * G) return;
+    const int g = L / a.T, t = L % a.T;
+    const int H = a.H, I = a.I, nblk = I / 32, nhb = I / 16;
+    const int row0 = g * R;
+    const int nrows = min(R, H - row0);
+    const int nsteps = (nrows + 3) / 4;
+
+    const int64_t p = (int64_t)t * a.topk + j;
+    const int e = a.topk_ids[p];
+    const bool ok = (unsigned)e < (unsigned)a.E;
+    const float wt = ok ? a.topk_weights[p] : 0.0f;
+    const int es = ok ? e : 0;
+    const rsrc_t rx = make_rsrc(a.h, (uint32_t)((int64_t)a.T * a.topk * I * 2));
+    const rsrc_t rw = make_rsrc(a.w2 + (int64_t)es * H * (I / 2), ok ? (uint32_t)((int64_t)H * (I / 2)) : 0u);
+    const rsrc_t rs = make_rsrc((const uint8_t*)a.w2_scale + (int64_t)es * H * nblk,
+                                ok ? (uint32_t)((int64_t)H * nblk) : 0u);
+    u32x4 x[NHC][2];
+    issue_xh<NHC>(x, rx, ok ? (uint32_t)p * (uint32_t)(2 * I) : kOob, nhb, lane);
+
+    auto consume = [&](const HalfRows<NHC>& W, uint8_t* lsc, int s) {
+        W.stage_scales(lsc, nhb, lane);
+        wave_lds_sync();
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+        half_dot<NHC>(W, lsc, x, nhb, lane, acc);
+        // Rows after reduce4: 4s + (0, 2, 1, 3) in 16-lane rows 0..3.
+        const float q = reduce4(acc);
+        const int rho = lane >> 4;
+        const int r = 4 * s + ((rho == 1) ? 2 : (rho == 2) ? 1 : rho);
+        if ((lane & 15) == 0 && r < nrows) red[j][r] = wt * q;
+    };
+    HalfRows<NHC> WA, WB;
+    WA.issue_run(rw, rs, row0, min(4, nrows), nhb, lane);
+    for (int s = 0; s < nsteps; s += 2) {
+        if (s + 1 < nsteps) WB.issue_run(rw, rs, row0 + 4 * (s + 1), min(4, nrows - 4 * (s + 1)), nhb, lane);
+        consume(WA, lds_scale[j][0], s);
+        if (s + 1 >= nsteps) break;
+        if (s + 2 < nsteps) WA.issue_run(rw, rs, row0 + 4 * (s + 2), min(4, nrows - 4 * (s + 2)), nhb, lane);
+        consume(WB, lds_scale[j][1], s + 1);
+    }
+    __syncthreads();
+    if ((int)threadIdx.x < nrows) {
+        float sum = 0.f;
+        for (int jj = 0; jj < a.topk; ++jj) sum += red[jj][threadIdx.x];
+        a.out[(int64_t)t * H + row0 + threadIdx.x] = f32_to_bf16_bits(sum);
+    }
+}
+
 bool gemv_eligible(const MoeGemmArgs& a) {
     const int max_rows = a.T < a.bm ? a.T : a.bm;
     return a.fmt == kFmtMxfp4 && max_rows <= 4 && a.topk <= kGemvWaves2 * kSlotsPerWave &&
@@ -306,10 +440,25 @@ hipError_t launch_gemv_stage(const MoeGemmArgs& a, int stage, hipStream_t s) {
         else if (rows <= 2) launch_stage1_nr<2>(a, nch, s);
         else launch_stage1_nr<4>(a, nch, s);
     } else {
-        const int nch = (a.I / 32 + 63) / 64;
-        const dim3 grid((unsigned)((int64_t)a.T * (a.H / 4))), block(kGemvWaves2 * 64);
-        if (nch == 1) hipLaunchKernelGGL((stage2_gemv_tok_kernel<1>), grid, block, 0, s, a);
-        else hipLaunchKernelGGL((stage2_gemv_tok_kernel<2>), grid, block, 0, s, a);
+        const int nhc = (a.I / 16 + 63) / 64;
+        if (nhc > 3) {
+            // I above 3072: the persistent kernel's registers would spill.
+            const int nch = (a.I / 32 + 63) / 64;
+            const dim3 grid((unsigned)((int64_t)a.T * (a.H / 4))), block(kGemvWaves2 * 64);
+            if (nch == 1) hipLaunchKernelGGL((stage2_gemv_tok_kernel<1>), grid, block, 0, s, a);
+            else hipLaunchKernelGGL((stage2_gemv_tok_kernel<2>), grid, block, 0, s, a);
+        } else {
+            // About one workgroup per CU: G runs of R rows per token.
+            int G = 256 / a.T;
+            int R = (a.H + G - 1) / G;
+            R = R < 4 ? 4 : R > kRowsMax ? kRowsMax : R;
+            G = (a.H + R - 1) / R;
+            const int64_t nwg = (int64_t)a.T * G;
+            const dim3 grid((unsigned)((nwg + 7) / 8 * 8)), block(a.topk * 64);
+            if (nhc == 1) hipLaunchKernelGGL((stage2_gemv_rows_kernel<1>), grid, block, 0, s, a, G, R);
+            else if (nhc == 2) hipLaunchKernelGGL((stage2_gemv_rows_kernel<2>), grid, block, 0, s, a, G, R);
+            else hipLaunchKernelGGL((stage2_gemv_rows_kernel<3>), grid, block, 0, s, a, G, R);
+        }
     }
     return hipGetLastError();
 }

@@ -239,12 +239,18 @@ def test_forward_ragged_shapes(moe, T, H, I, E, topk, bm):
     check_close_bf16_out(out_f64(out), ref, f"T={T} H={H} I={I} E={E} k={topk} bm={bm}")
 
 
-@pytest.mark.parametrize("T,E,topk", [(1, 8, 3), (2, 6, 4), (3, 5, 5), (4, 16, 2)])
-def test_forward_gemv_path_small(moe, T, E, topk):
+@pytest.mark.parametrize("T,E,topk,H,I", [
+    (1, 8, 3, 512, 1024), (2, 6, 4, 512, 1024), (3, 5, 5, 512, 1024), (4, 16, 2, 512, 1024),
+    (1, 8, 3, 512, 2048),    # two 64-lane chunks of half-blocks in the down kernel
+    (2, 5, 5, 1024, 1536),   # the second chunk half used
+    (3, 6, 4, 512, 3072),    # three chunks; runs of 7 down rows end in a partial 4-row step
+    (4, 16, 16, 512, 3072),  # 16 slots: one wave per slot, 1024 threads
+    (1, 6, 4, 512, 4096),    # I above 3072: the 8-wave down kernel
+])
+def test_forward_gemv_path_small(moe, T, E, topk, H, I):
     """Decode blocks of at most 4 token rows with K a multiple of 512 take the
-    GEMV-shaped kernels; H=512, I=1024 keeps the oracle fast."""
-    H, I = 512, 1024
-    wl = synth.small(T=T, H=H, I=I, E=E, topk=topk, seed=40 + T)
+    GEMV-shaped kernels; H=512 keeps the oracle fast."""
+    wl = synth.small(T=T, H=H, I=I, E=E, topk=topk, seed=40 + T + I)
     out = run_layer(moe, wl, topk)
     ids, w = oracle.route_topk(wl.logits, topk)
     ref = oracle.moe_forward(wl.x, wl.w13, wl.w13_scale, wl.w2, wl.w2_scale, 0, ids, w, I=I)
