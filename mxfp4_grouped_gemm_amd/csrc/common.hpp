@@ -115,6 +115,14 @@ __device__ __forceinline__ u32x2 bld8(rsrc_t r, uint32_t off) {
     return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
 }
 
+// Orders one wave's LDS writes before its later LDS reads (LDS executes a
+// wave's operations in order; this keeps the compiler from reordering them).
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // silu(g) * u in fp32. For very negative g, expf(-g) overflows to +inf and
 // the quotient is -0 (never NaN).
 __device__ __forceinline__ float swiglu(float g, float u) {

@@ -105,12 +105,6 @@ struct GemvWeights {
     }
 };
 
-__device__ __forceinline__ void wave_lds_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
 template <int NCH>
 __device__ __forceinline__ void issue_x(u32x4 (&x)[NCH][4], rsrc_t rx, uint32_t x_off, int nblk, int lane) {
 #pragma unroll

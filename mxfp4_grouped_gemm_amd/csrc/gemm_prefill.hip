@@ -55,6 +55,10 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 // tile) and 64 rows x 8 e8m0 bytes.
 constexpr int kPfWRows = 64;
 constexpr int kPfStage = 4;  // chunks per weight stage
+// Single-wave tiles up to this many tokens (at most one 32-row block per
+// expert needs T <= 32; above 16 tokens blocks fill up and the 4-wave tiles,
+// which share each activation chunk between four waves, are faster).
+constexpr int kPfDirectMaxTokens = 16;
 template <int NBMAX>
 struct __attribute__((aligned(16))) PfShared {
     uint8_t a[kPfABufs][NBMAX * kPfBlockRows * kPfRowBytes];
@@ -62,6 +66,19 @@ struct __attribute__((aligned(16))) PfShared {
     uint8_t bs[4][kPfWRows * 16];
     int32_t rows[NBMAX * kPfBlockRows];  // sorted_ids of the super-block
 };
+
+// Single-wave workgroups (one 32-row block each): the wave's weight stage
+// and the block's sorted ids only; activations go straight to registers.
+struct __attribute__((aligned(16))) PfSharedDirect {
+    uint8_t b[1][kPfWRows * 128];
+    uint8_t bs[1][kPfWRows * 16];
+    int32_t rows[kPfBlockRows];
+};
+
+// The shared activation buffer `buf` (none in single-wave workgroups).
+template <int NBMAX>
+__device__ __forceinline__ uint8_t* a_buf(PfShared<NBMAX>& sh, int buf) { return sh.a[buf]; }
+__device__ __forceinline__ uint8_t* a_buf(PfSharedDirect&, int) { return nullptr; }
 
 __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -135,8 +152,12 @@ __global__ __launch_bounds__(1024) void superblock_kernel(const int32_t* __restr
 //            -> h[sorted row] (bf16).
 //   STAGE 2: A = h rows (contiguous), K = I; wave w owns columns
 //            n0+64w.. +64 of w2; epilogue y[pair] (fp32).
-template <int STAGE, int FMT, int NB, int NBMAX>
-__device__ __forceinline__ void pf_tile(const MoeGemmArgs& a, PfShared<NBMAX>& sh, int e, int row0, int n0) {
+//   DIRECT: a single-wave workgroup and one 32-row block (NB = 1): the wave
+//            loads its MFMA activation operands straight from global memory
+//            (L2) into a ring of registers, so there is no shared tile and
+//            no workgroup barrier; the wave streams its weights on its own.
+template <int STAGE, int FMT, int NB, bool DIRECT, class SH>
+__device__ __forceinline__ void pf_tile(const MoeGemmArgs& a, SH& sh, int e, int row0, int n0) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -150,9 +171,23 @@ __device__ __forceinline__ void pf_tile(const MoeGemmArgs& a, PfShared<NBMAX>& s
     const int arow = tid >> 3;
     const int apiece = tid & 7;
     const uint32_t lds_w = (uint32_t)arow * kPfRowBytes + (uint32_t)((apiece ^ ((arow >> 1) & 7)) << 4);
+    const int half = lane >> 5;
+    const int nl = lane & 31;
     rsrc_t ra;
     uint32_t aoff[NB];
-    if (STAGE == 1) {
+    if constexpr (DIRECT) {
+        // Lane (nl, half): row nl of the block, logical pieces 4*half.. of a
+        // chunk (the operand order of the MFMA k-steps).
+        static_assert(NB == 1, "direct tiles hold one block");
+        const int p = sh.rows[nl];
+        if (STAGE == 1) {
+            ra = make_rsrc(a.x, (uint32_t)((int64_t)a.T * a.H * 2));
+            aoff[0] = (p >= 0 && p < P) ? (uint32_t)(p / a.topk) * (uint32_t)(2 * a.H) + 64u * half : kOob;
+        } else {
+            ra = make_rsrc(a.h, (uint32_t)(a.cap * a.I * 2));
+            aoff[0] = (p >= 0 && p < P) ? (uint32_t)(row0 + nl) * (uint32_t)(2 * a.I) + 64u * half : kOob;
+        }
+    } else if constexpr (STAGE == 1) {
         ra = make_rsrc(a.x, (uint32_t)((int64_t)a.T * a.H * 2));
 #pragma unroll
         for (int i = 0; i < NB; ++i) {
@@ -169,8 +204,6 @@ __device__ __forceinline__ void pf_tile(const MoeGemmArgs& a, PfShared<NBMAX>& s
     // --- weights. Staging row r (0..63) of wave w: block r / 32 of the wave
     // (stage 1: gate columns n0+32w.., then the matching up rows; stage 2:
     // columns n0+64w..+64), row r % 32 of it.
-    const int half = lane >> 5;
-    const int nl = lane & 31;
     rsrc_t rw, rs;
     auto grow = [&](int r) -> uint32_t {
         if (STAGE == 1) return (uint32_t)((r < 32 ? 0 : a.I) + n0 + 32 * w + (r & 31));
@@ -268,16 +301,27 @@ __device__ __forceinline__ void pf_tile(const MoeGemmArgs& a, PfShared<NBMAX>& s
         for (int i = 0; i < NB; ++i)
             ar[slot][i] = bld16(ra, (ok && aoff[i] != kOob) ? aoff[i] + (uint32_t)(kPfRowBytes * c) : kOob);
     };
+    // DIRECT: chunk c's four k-step operands sit in ring slot c % DD from
+    // their load (issued when chunk c - DD finished with the slot) to the
+    // chunk's MFMAs. A ring of a whole stage: the oldest activation load is
+    // never younger than the weight stage that the next store waits for.
+    constexpr int DD = 4;
+    u32x4 ad[DIRECT ? DD : 1][4];
+    auto issue_ad = [&](int slot, int c) {
+        const bool ok = c < nchunks && aoff[0] != kOob;
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) ad[slot][s4] = bld16(ra, ok ? aoff[0] + (uint32_t)(kPfRowBytes * c + 16 * s4) : kOob);
+    };
     auto store_a = [&](int slot, int buf) {
 #pragma unroll
         for (int i = 0; i < NB; ++i)
-            *(u32x4*)(&sh.a[buf][32 * i * kPfRowBytes + lds_w]) = ar[slot][i];
+            *(u32x4*)(a_buf(sh, buf) + 32 * i * kPfRowBytes + lds_w) = ar[slot][i];
     };
     // MFMA A operand from LDS: row 32i + nl, logical piece 4*half + s.
     const int sw = (nl >> 1) & 7;
     bf16x8 av[2][NB];
     auto read_a = [&](int dst, int buf, int s) {
-        const uint8_t* base = sh.a[buf] + nl * kPfRowBytes + (((4 * half + s) ^ sw) << 4);
+        const uint8_t* base = a_buf(sh, buf) + nl * kPfRowBytes + (((4 * half + s) ^ sw) << 4);
 #pragma unroll
         for (int i = 0; i < NB; ++i) av[dst][i] = *(const bf16x8*)(base + 32 * i * kPfRowBytes);
     };
@@ -297,32 +341,42 @@ __device__ __forceinline__ void pf_tile(const MoeGemmArgs& a, PfShared<NBMAX>& s
     // Weights: stage t (chunks 4t..4t+3) is written to the wave's LDS in
     // chunk 4t-2, after the last read of stage t-1 (chunk 4t-1's operands,
     // read one chunk ahead); stage t+1 is then loaded into the registers.
-    issue_a(0, 0);
-    issue_a(1, 1);
-    issue_bstage(0, 0);
-    store_a(0, 0);
-    store_a(1, 1);
-    store_bstage(0);
+    if constexpr (DIRECT) {
 #pragma unroll
-    for (int t = 1; t <= BR; ++t) issue_bstage(t % BR, t);
+        for (int k = 0; k < DD; ++k) issue_ad(k, k);
+        issue_bstage(0, 0);
+        store_bstage(0);
 #pragma unroll
-    for (int k = 2; k < 2 + DA; ++k) issue_a(k % DA, k);
-    __syncthreads();
+        for (int t = 1; t <= BR; ++t) issue_bstage(t % BR, t);
+        wave_lds_sync();
+    } else {
+        issue_a(0, 0);
+        issue_a(1, 1);
+        issue_bstage(0, 0);
+        store_a(0, 0);
+        store_a(1, 1);
+        store_bstage(0);
+#pragma unroll
+        for (int t = 1; t <= BR; ++t) issue_bstage(t % BR, t);
+#pragma unroll
+        for (int k = 2; k < 2 + DA; ++k) issue_a(k % DA, k);
+        __syncthreads();
+    }
     // Small tiles (1-2 blocks) have too few MFMAs per k-step to cover an LDS
     // read between consecutive steps: they read a whole chunk's operands one
     // chunk ahead instead.
-    constexpr bool CP = NB <= 2 && FMT == kFmtMxfp4;
+    constexpr bool CP = NB <= 2 && FMT == kFmtMxfp4 && !DIRECT;
     bf16x8 avc[4][NB], avn[4][NB];
     auto read_a_chunk = [&](bf16x8 (&dst)[4][NB], int buf) {
 #pragma unroll
         for (int s4 = 0; s4 < 4; ++s4) {
-            const uint8_t* base = sh.a[buf] + nl * kPfRowBytes + (((4 * half + s4) ^ sw) << 4);
+            const uint8_t* base = a_buf(sh, buf) + nl * kPfRowBytes + (((4 * half + s4) ^ sw) << 4);
 #pragma unroll
             for (int i = 0; i < NB; ++i) dst[s4][i] = *(const bf16x8*)(base + 32 * i * kPfRowBytes);
         }
     };
     if (CP) read_a_chunk(avc, 0);
-    else read_a(0, 0, 0);
+    else if (!DIRECT) read_a(0, 0, 0);
     u32x4 bcur[2], bnext[2];
     svec scur[2], snext[2];
     read_scales(scur);
@@ -355,8 +409,10 @@ __device__ __forceinline__ void pf_tile(const MoeGemmArgs& a, PfShared<NBMAX>& s
                         read_bchunk(bnext, 0);
                         read_scales(snext);
                     }
-                    store_a((u + 2) % DA, buf2);  // A(c+2)
-                    issue_a((u + 2) % DA, c + 2 + DA);
+                    if (!DIRECT) {
+                        store_a((u + 2) % DA, buf2);  // A(c+2)
+                        issue_a((u + 2) % DA, c + 2 + DA);
+                    }
                     if (u == 2) {  // next stage into LDS, its slot reloaded BR stages ahead
                         const int slot = (tslot + 1) % BR;
                         store_bstage(slot);
@@ -367,18 +423,19 @@ __device__ __forceinline__ void pf_tile(const MoeGemmArgs& a, PfShared<NBMAX>& s
                 // Operands of the next k-step (the next chunk's first at s = 3).
                 Bop n0, n1;
                 if (s < 3) {
-                    if (!CP) read_a((s + 1) & 1, buf, s + 1);
+                    if (!CP && !DIRECT) read_a((s + 1) & 1, buf, s + 1);
                     n0 = decode(bcur[0][s + 1], sc0);
                     n1 = decode(bcur[1][s + 1], sc1);
                 } else {
-                    if (!CP) read_a(0, buf1, 0);
+                    if (!CP && !DIRECT) read_a(0, buf1, 0);
                     const svec* sn = u < 3 ? scur : snext;
                     n0 = decode(bnext[0][0], scale_of(sn[0], (u + 1) & 3));
                     n1 = decode(bnext[1][0], scale_of(sn[1], (u + 1) & 3));
                 }
 #pragma unroll
                 for (int i = 0; i < NB; ++i) {
-                    const bf16x8 ai = CP ? avc[s][i] : av[s & 1][i];
+                    const bf16x8 ai = DIRECT ? __builtin_bit_cast(bf16x8, ad[u % DD][s])
+                                             : CP ? avc[s][i] : av[s & 1][i];
                     acc[i][0] = mfma32(ai, b0.hi, acc[i][0]);
                     acc[i][1] = mfma32(ai, b1.hi, acc[i][1]);
                     if constexpr (FMT != kFmtMxfp4) {
@@ -421,8 +478,14 @@ __device__ __forceinline__ void pf_tile(const MoeGemmArgs& a, PfShared<NBMAX>& s
             // operand reads, issued in the k-step just before) must be
             // complete; those reads stay in flight across the barrier.
             // (With chunk-level reads every LDS operation completes first.)
-            if (CP) __syncthreads();
-            else asm volatile("s_waitcnt lgkmcnt(%0)\n\ts_barrier" ::"n"(NB) : "memory");
+            if (DIRECT) {
+                issue_ad(u % DD, c + DD);  // the slot this chunk used
+                wave_lds_sync();
+            } else if (CP) {
+                __syncthreads();
+            } else {
+                asm volatile("s_waitcnt lgkmcnt(%0)\n\ts_barrier" ::"n"(NB) : "memory");
+            }
             buf = buf1;
         }
     }
@@ -481,20 +544,43 @@ __global__ __launch_bounds__(kPfThreads, NBMAX <= 2 ? 2 : 1) void prefill_kernel
     __syncthreads();
     const int n0 = nt * (STAGE == 1 ? 128 : 256);
     if constexpr (NBMAX <= 2) {
-        if (nb == 1) pf_tile<STAGE, FMT, 1>(a, sh, e, row0, n0);
-        else pf_tile<STAGE, FMT, 2>(a, sh, e, row0, n0);
+        if (nb == 1) pf_tile<STAGE, FMT, 1, false>(a, sh, e, row0, n0);
+        else pf_tile<STAGE, FMT, 2, false>(a, sh, e, row0, n0);
     } else {
         switch (nb) {
-            case 1: pf_tile<STAGE, FMT, 1>(a, sh, e, row0, n0); break;
-            case 2: pf_tile<STAGE, FMT, 2>(a, sh, e, row0, n0); break;
-            case 3: pf_tile<STAGE, FMT, 3>(a, sh, e, row0, n0); break;
-            case 4: pf_tile<STAGE, FMT, 4>(a, sh, e, row0, n0); break;
-            case 5: pf_tile<STAGE, FMT, 5>(a, sh, e, row0, n0); break;
-            case 6: pf_tile<STAGE, FMT, 6>(a, sh, e, row0, n0); break;
-            case 7: pf_tile<STAGE, FMT, 7>(a, sh, e, row0, n0); break;
-            default: pf_tile<STAGE, FMT, 8>(a, sh, e, row0, n0); break;
+            case 1: pf_tile<STAGE, FMT, 1, false>(a, sh, e, row0, n0); break;
+            case 2: pf_tile<STAGE, FMT, 2, false>(a, sh, e, row0, n0); break;
+            case 3: pf_tile<STAGE, FMT, 3, false>(a, sh, e, row0, n0); break;
+            case 4: pf_tile<STAGE, FMT, 4, false>(a, sh, e, row0, n0); break;
+            case 5: pf_tile<STAGE, FMT, 5, false>(a, sh, e, row0, n0); break;
+            case 6: pf_tile<STAGE, FMT, 6, false>(a, sh, e, row0, n0); break;
+            case 7: pf_tile<STAGE, FMT, 7, false>(a, sh, e, row0, n0); break;
+            default: pf_tile<STAGE, FMT, 8, false>(a, sh, e, row0, n0); break;
         }
     }
+}
+
+// One workgroup per (32-row block, 64 weight rows), for small batches: a
+// token routes to an expert at most once, so with T <= 32 no expert holds
+// more than one block and the blocks are the whole work list (no super-block
+// pass). Correct for any block list; an expert with several blocks would
+// just stream its weights once per block.
+template <int STAGE, int FMT>
+__global__ __launch_bounds__(64) void prefill_direct_kernel(MoeGemmArgs a, int nblocks, int ntiles) {
+    __shared__ PfSharedDirect sh;
+    // Workgroup ids go round-robin over the 8 XCDs: block blk lives on XCD
+    // blk % 8 with all of its N tiles, so its activation rows stay in one L2.
+    const int b = blockIdx.x;
+    const int xcd = b & 7, j = b >> 3;
+    const int blk = 8 * (j / ntiles) + xcd;
+    const int nt = j % ntiles;
+    if (blk >= nblocks) return;
+    const int e = a.block_expert[blk];
+    if (e < 0 || e >= a.E) return;
+    const int row0 = blk * kPfBlockRows;
+    if (threadIdx.x < kPfBlockRows) sh.rows[threadIdx.x] = a.sorted_ids[row0 + threadIdx.x];
+    wave_lds_sync();
+    pf_tile<STAGE, FMT, 1, true>(a, sh, e, row0, nt * (STAGE == 1 ? 32 : 64));
 }
 
 bool prefill_eligible(const MoeGemmArgs& a) {
@@ -510,6 +596,18 @@ int64_t prefill_list_bytes(int64_t cap) { return (cap / kPfBlockRows + 1) * 16 +
 hipError_t launch_prefill(const MoeGemmArgs& a, int stage, void* list_ws, hipStream_t s) {
     int4* list = (int4*)list_ws;
     const int64_t nblocks = a.cap / kPfBlockRows;
+    if (a.T <= kPfDirectMaxTokens) {
+        const int ntiles = stage == 1 ? a.I / 32 : a.H / 64;
+        const dim3 grid((unsigned)(8 * ((nblocks + 7) / 8) * ntiles)), block(64);
+        if (a.fmt == kFmtMxfp4) {
+            if (stage == 1) hipLaunchKernelGGL((prefill_direct_kernel<1, kFmtMxfp4>), grid, block, 0, s, a, (int)nblocks, ntiles);
+            else hipLaunchKernelGGL((prefill_direct_kernel<2, kFmtMxfp4>), grid, block, 0, s, a, (int)nblocks, ntiles);
+        } else {
+            if (stage == 1) hipLaunchKernelGGL((prefill_direct_kernel<1, kFmtInt4g32>), grid, block, 0, s, a, (int)nblocks, ntiles);
+            else hipLaunchKernelGGL((prefill_direct_kernel<2, kFmtInt4g32>), grid, block, 0, s, a, (int)nblocks, ntiles);
+        }
+        return hipGetLastError();
+    }
     int* count = (int*)(list + nblocks);
     // Few rows per expert (decode batches): 64-row super-blocks and a small
     // LDS footprint, so two workgroups share a CU and keep more weight bytes

@@ -281,6 +281,34 @@ def test_forward_prefill_path(moe, T, H, I, E, topk, hot):
           f"max|ref| {np.abs(ref).max() / rms:.1f} RMS")
 
 
+@pytest.mark.parametrize("T,H,I,E,topk,hot,fmt", [
+    (8, 512, 256, 8, 4, 0, 0),     # 32 pairs: the smallest batch on these kernels
+    (16, 256, 512, 16, 6, 0, 0),   # every expert one block, most rows padding
+    (13, 768, 256, 4, 3, 0, 0),    # ragged T
+    (16, 512, 256, 12, 3, 3, 0),   # skewed: hot experts hold every token
+    (16, 512, 512, 8, 4, 0, 1),    # int4-g32 weights
+    (32, 512, 256, 12, 3, 3, 0),   # 17..32 tokens: the 4-wave tiles, 2-block super-blocks
+])
+def test_forward_direct_tiles(moe, T, H, I, E, topk, hot, fmt):
+    """Batches of 5..16 tokens (at least 32 pairs, 32-row blocks) take
+    single-wave MFMA tiles, one per (block, 64 weight rows); every token is
+    compared."""
+    wl = synth.small(T=T, H=H, I=I, E=E, topk=topk, seed=11 * T + E + fmt, hot=hot)
+    assert moe.moe_default_block_m(T, topk, E) == 32
+    ids, w = oracle.route_topk(wl.logits, topk)
+    if fmt == 0:
+        out = run_layer(moe, wl, topk)
+        ref = oracle.moe_forward(wl.x, wl.w13, wl.w13_scale, wl.w2, wl.w2_scale, 0, ids, w, I=I)
+    else:
+        q13, s13 = moe.requantize_mxfp4_experts(dev(wl.w13), dev(wl.w13_scale))
+        q2, s2 = moe.requantize_mxfp4_experts(dev(wl.w2), dev(wl.w2_scale))
+        out = run_layer(moe, wl, topk, fmt=1, w=(q13, s13, q2, s2))
+        rq13, rs13 = oracle.requant_int4g32(wl.w13, wl.w13_scale)
+        rq2, rs2 = oracle.requant_int4g32(wl.w2, wl.w2_scale)
+        ref = oracle.moe_forward(wl.x, rq13, rs13, rq2, rs2, 1, ids, w, I=I)
+    check_close_bf16_out(out_f64(out), ref, f"direct T={T} H={H} I={I} E={E} k={topk} hot={hot} fmt={fmt}")
+
+
 def test_int4_forward_prefill_path(moe):
     """int4-g32 weights on the LDS-tiled MFMA kernels: requantize on the GPU
     (bit-exact against the oracle elsewhere), then compare the whole layer
