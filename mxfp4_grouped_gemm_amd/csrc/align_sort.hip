@@ -14,8 +14,8 @@
 // route_align_kernel runs the routing of up to 64 tokens (route.hpp, one
 // wave per token) in the same workgroup and sorts straight from LDS, saving
 // a launch and a round trip of the ids through memory at decode sizes;
-// route_align_small_kernel does the same for up to 64 pairs with a one-wave
-// sort.
+// route_align_small_kernel does the same for up to 4 tokens and 64 pairs with
+// a one-wave sort.
 #include "common.hpp"
 #include "launch.hpp"
 #include "route.hpp"
@@ -138,14 +138,18 @@ __global__ __launch_bounds__(kSortThreads) void route_align_kernel(
                     num_post_pad);
 }
 
-// Up to 64 pairs: route with up to four waves, then one wave sorts with
-// one pair per lane and no workgroup barrier after the routing. A pair's
-// position is (padded start of its expert) + (pairs of the same expert
-// before it), both counted over the wave with readlane loops; the padded
-// start of an expert sums the padded lengths of the smaller experts present.
+// Up to 4 tokens and 64 pairs: four waves route a token each while the
+// workgroup clears the LDS tables, then one wave sorts (a pair per lane)
+// without loops over pairs. A token routes to an expert at most once, so an expert's pairs are
+// a bitmask of tokens: the count is its popcount and a pair's rank within
+// the expert is the popcount of the lower tokens (pairs of one expert are in
+// token order, which is pair order). Padded segment starts come from one
+// wave scan over the experts (lane l owns experts VPL*l ..); sorted_ids and
+// block_expert are assembled in LDS and copied out with coalesced stores.
 // Same outputs as align_sort_body.
+constexpr int kSmallTokens = 4;
 constexpr int kSmallPairs = 64;
-constexpr int kSmallPairsFused = 16;  // measured: above this the 1024-thread sort is faster
+constexpr int64_t kSmallCapMax = 4096;  // e.g. 64 pairs at block_m 64, 16 at 256
 
 template <int VPL>
 __global__ __launch_bounds__(256) void route_align_small_kernel(
@@ -154,51 +158,63 @@ __global__ __launch_bounds__(256) void route_align_small_kernel(
     int32_t* __restrict__ block_expert, int32_t* __restrict__ expert_offsets,
     int32_t* __restrict__ num_post_pad) {
     __shared__ int32_t ids_lds[kSmallPairs];
+    __shared__ uint32_t tokens[kMaxExperts];
+    __shared__ int32_t start[kMaxExperts];
+    __shared__ int32_t srt[kSmallCapMax];
+    __shared__ int32_t blk[kSmallCapMax / 16];
     const int wv = threadIdx.x >> 6;
     const int lane = threadIdx.x & 63;
+    const int P = T * topk;
+    const int ncap = (int)cap, nblk = (int)(cap / bm);
+    for (int i = threadIdx.x; i < E; i += 256) tokens[i] = 0u;
+    for (int i = threadIdx.x; i < ncap; i += 256) srt[i] = P;
+    for (int i = threadIdx.x; i < nblk; i += 256) blk[i] = -1;
     for (int t = wv; t < T; t += 4)
         route_token<VPL>(logits + (int64_t)t * E, E, topk, renorm, ids + (int64_t)t * topk,
                          weights + (int64_t)t * topk, ids_lds + t * topk);
     __syncthreads();
     if (wv != 0) return;
-    const int P = T * topk;
-    const int e = lane < P ? ids_lds[lane] : -1;
-    const bool valid = (unsigned)e < (unsigned)E;
-    int cnt = 0, before = 0;
-    for (int q = 0; q < P; ++q) {
-        const int eq = __builtin_amdgcn_readlane(e, q);
-        const bool same = valid && eq == e;
-        cnt += same ? 1 : 0;
-        before += (same && q < lane) ? 1 : 0;
+    const int pe = lane < P ? ids_lds[lane] : -1;
+    const bool valid = (unsigned)pe < (unsigned)E;
+    const int pt = lane / topk;
+    if (valid) atomicOr(&tokens[pe], 1u << pt);
+    wave_lds_sync();
+    // Padded lengths of this lane's experts and their exclusive prefix.
+    int len[VPL], pad[VPL], local = 0;
+#pragma unroll
+    for (int c = 0; c < VPL; ++c) {
+        const int x = VPL * lane + c;
+        len[c] = x < E ? __popc(tokens[x]) : 0;
+        pad[c] = (len[c] + bm - 1) & -bm;  // block_m is a power of two
+        local += pad[c];
     }
-    const bool leader = valid && before == 0;
-    const int padded = (cnt + bm - 1) / bm * bm;
-    const uint64_t leaders = __ballot(leader);
-    // Padded start of this lane's expert, and the total.
-    int start = 0, total = 0;
-    for (uint64_t m = leaders; m; m &= m - 1ull) {
-        const int q = __ffsll((unsigned long long)m) - 1;
-        const int eq = __builtin_amdgcn_readlane(e, q);
-        const int pq = __builtin_amdgcn_readlane(padded, q);
-        start += (valid && eq < e) ? pq : 0;
-        total += pq;
+    int incl = local;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int o = __shfl_up(incl, off);
+        if (lane >= off) incl += o;
     }
-    if (valid) sorted_ids[start + before] = lane;
-    if (leader) {
-        for (int r = start + cnt; r < start + padded; ++r) sorted_ids[r] = P;
-        for (int b = start / bm; b < (start + padded) / bm; ++b) block_expert[b] = e;
-    }
-    for (int64_t r = total + lane; r < cap; r += 64) sorted_ids[r] = P;
-    for (int64_t b = total / bm + lane; b < cap / bm; b += 64) block_expert[b] = -1;
-    for (int x = lane; x <= E; x += 64) {
-        int off = 0;
-        for (uint64_t m = leaders; m; m &= m - 1ull) {
-            const int q = __ffsll((unsigned long long)m) - 1;
-            off += __builtin_amdgcn_readlane(e, q) < x ? __builtin_amdgcn_readlane(padded, q) : 0;
+    const int total = __shfl(incl, 63);
+    int base = incl - local;
+#pragma unroll
+    for (int c = 0; c < VPL; ++c) {
+        const int x = VPL * lane + c;
+        if (x < E) {
+            expert_offsets[x] = base;
+            start[x] = base;
+            for (int b = base / bm; b < (base + pad[c]) / bm; ++b) blk[b] = x;
         }
-        expert_offsets[x] = off;
+        base += pad[c];
     }
-    if (lane == 0) num_post_pad[0] = total;
+    if (lane == 0) {
+        expert_offsets[E] = total;
+        num_post_pad[0] = total;
+    }
+    wave_lds_sync();
+    if (valid) srt[start[pe] + __popc(tokens[pe] & ((1u << pt) - 1u))] = lane;
+    wave_lds_sync();
+    for (int i = lane; i < ncap; i += 64) sorted_ids[i] = srt[i];
+    for (int i = lane; i < nblk; i += 64) block_expert[i] = blk[i];
 }
 
 hipError_t launch_align_sort(const int32_t* ids, int P, int E, int bm, int64_t cap,
@@ -221,7 +237,7 @@ hipError_t launch_route_align(const float* logits, int T, int E, int topk, int r
     const int vpl = (E + 63) / 64;
 #define MOE_LAUNCH_RA(V)                                                                                 \
     do {                                                                                                 \
-        if ((int64_t)T * topk <= kSmallPairsFused)                                                       \
+        if (T <= kSmallTokens && T * topk <= kSmallPairs && cap <= kSmallCapMax)                         \
             hipLaunchKernelGGL(route_align_small_kernel<V>, dim3(1), dim3(256), 0, s, logits, T, E, topk, \
                                renorm, bm, cap, ids, weights, sorted_ids, block_expert, expert_offsets,  \
                                num_post_pad);                                                            \

@@ -5,8 +5,8 @@
 // topk (equal logits: lower index first), weight them by their softmax
 // probabilities, renormalised over the kept experts on request.
 //
-// Selection is a radix select over order-preserving 32-bit keys: 32 rounds of
-// (compare, ballot, popcount) find the k-th largest key; keys above it are
+// Selection is a radix select over order-preserving 32-bit keys: 16 rounds of
+// (compare, ballot, popcount) over two key bits find the k-th largest key; keys above it are
 // kept and the ties at it are taken lowest index first. The kept experts are
 // then ranked against each other in a scalar loop of at most topk steps.
 // Everything stays in registers and SGPRs; no cross-lane shuffles through LDS.
@@ -46,14 +46,24 @@ __device__ __forceinline__ void route_token(const float* __restrict__ row, int E
         val[i] = ok[i] ? row[e] : 0.0f;
         key[i] = route_key(val[i]);
     }
-    // k-th largest key: the largest T with count(key >= T) >= topk.
-    uint32_t thr = 0u;
-    for (int bit = 31; bit >= 0; --bit) {
-        const uint32_t cand = thr | (1u << bit);
-        int cnt = 0;
+    // k-th largest key: the largest T with count(key >= T) >= topk, two key
+    // bits per round (three independent counts). Slots past E get key 0,
+    // which no candidate (always >= 1) counts.
+    uint32_t kv[VPL];
 #pragma unroll
-        for (int i = 0; i < VPL; ++i) cnt += wave_popc(ok[i] && key[i] >= cand);
-        if (cnt >= topk) thr = cand;
+    for (int i = 0; i < VPL; ++i) kv[i] = ok[i] ? key[i] : 0u;
+    uint32_t thr = 0u;
+#pragma unroll
+    for (int bit = 30; bit >= 0; bit -= 2) {
+        const uint32_t c1 = thr | (1u << bit), c2 = thr | (2u << bit), c3 = thr | (3u << bit);
+        int n1 = 0, n2 = 0, n3 = 0;
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) {
+            n1 += __popcll(__builtin_amdgcn_ballot_w64(kv[i] >= c1));
+            n2 += __popcll(__builtin_amdgcn_ballot_w64(kv[i] >= c2));
+            n3 += __popcll(__builtin_amdgcn_ballot_w64(kv[i] >= c3));
+        }
+        thr = n3 >= topk ? c3 : n2 >= topk ? c2 : n1 >= topk ? c1 : thr;
     }
     int above = 0;
 #pragma unroll

@@ -174,22 +174,25 @@ def test_route_align_matches_oracle(moe, name, bm):
 
 
 @pytest.mark.parametrize("T,E,topk", [(1, 1024, 16), (2, 8, 8), (4, 6, 4), (16, 8, 1), (1, 112, 15),
-                                      (1, 1024, 64), (4, 8, 8), (3, 20, 7), (4, 112, 15)])
-@pytest.mark.parametrize("bm", [16, 32])
+                                      (16, 1024, 1), (1, 1024, 64), (4, 8, 8), (3, 20, 7), (4, 112, 15)])
+@pytest.mark.parametrize("bm", [16, 32, 256])
 def test_route_align_small_matches_oracle(moe, T, E, topk, bm):
     """Small token counts: up to 16 pairs the fused call sorts with a single
-    wave (experts shared by several tokens, every expert chosen, E = 1024),
-    above that with the workgroup sort."""
+    wave (experts shared by several tokens, every expert chosen, E = 1024,
+    16 tokens, block_m up to 256), above that with the workgroup sort. The
+    whole capacity is compared (sentinel P and block -1 past the used part)."""
     spec = synth.Spec("adhoc", T=T, H=256, I=128, E=E, topk=topk, seed=300 + T * E + topk)
     wl = synth.make(spec, with_weights=False)
     ids, w, s, be, off, npp = moe.moe_route_align(dev(wl.logits), topk, E, bm)
     torch.cuda.synchronize()
     rids, rw = oracle.route_topk(wl.logits, topk)
     assert np.array_equal(ids.cpu().numpy(), rids)
+    np.testing.assert_allclose(w.cpu().numpy(), rw, rtol=1e-6, atol=1e-7)
     rs, rbe, roff, rnpp = oracle.align_sort(rids, E, bm)
     assert int(npp.item()) == rnpp
-    assert np.array_equal(s.cpu().numpy()[:len(rs)], rs)
-    assert np.array_equal(be.cpu().numpy()[:len(rs) // bm], rbe)
+    s_np, be_np = s.cpu().numpy(), be.cpu().numpy()
+    assert len(rs) == len(s_np) and np.array_equal(s_np, rs)
+    assert np.array_equal(be_np, rbe)
     assert np.array_equal(off.cpu().numpy(), roff)
 
 
