@@ -114,6 +114,16 @@ __device__ __forceinline__ u32x4 bld16(rsrc_t r, uint32_t off) {
 __device__ __forceinline__ u32x2 bld8(rsrc_t r, uint32_t off) {
     return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
 }
+// The same with a wave-uniform part of the offset in the scalar operand
+// (no per-lane address arithmetic). Only the vector part is checked against
+// the record count, so callers keep every access inside the buffer (the
+// scalar part is clamped) and put kOob in the vector part to mask a lane.
+__device__ __forceinline__ u32x4 bld16s(rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+__device__ __forceinline__ u32x2 bld8s(rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+}
 
 // Orders one wave's LDS writes before its later LDS reads (LDS executes a
 // wave's operations in order; this keeps the compiler from reordering them).

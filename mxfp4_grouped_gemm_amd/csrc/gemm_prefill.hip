@@ -234,14 +234,16 @@ __device__ __forceinline__ void pf_tile(const MoeGemmArgs& a, SH& sh, int e, int
     using svec = typename std::conditional<FMT == kFmtMxfp4, u32x2, u32x4>::type;
     constexpr int SVB = (int)sizeof(svec);
     svec sraw[BR];
+    // The stage advance is a scalar offset; stages past the end (never
+    // consumed) are not loaded (a uniform branch).
     auto issue_bstage = [&](int slot, int st) {
-        const bool ok = st < nstages;
+        if (st >= nstages) return;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) braw[slot][j] = bld16(rw, ok ? boff[j] + 128u * st : kOob);
+        for (int j = 0; j < 8; ++j) braw[slot][j] = bld16s(rw, boff[j], 128u * st);
         if constexpr (FMT == kFmtMxfp4)
-            sraw[slot] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, ok ? soff + 8u * st : kOob, 0, 0));
+            sraw[slot] = bld8s(rs, soff, 8u * st);
         else
-            sraw[slot] = bld16(rs, ok ? soff + 16u * st : kOob);
+            sraw[slot] = bld16s(rs, soff, 16u * st);
     };
     uint8_t* const wl = sh.b[w];
     uint8_t* const sl = sh.bs[w];
@@ -295,11 +297,12 @@ __device__ __forceinline__ void pf_tile(const MoeGemmArgs& a, SH& sh, int e, int
     // out-of-range offsets (zeros, no traffic).
     constexpr int DA = (NB >= 3 && NB <= 6 && FMT == kFmtMxfp4) ? 4 : 2;
     u32x4 ar[DA][NB];
+    // Chunks past the end re-read the last one (never consumed); padding
+    // rows carry kOob in the vector offset.
     auto issue_a = [&](int slot, int c) {
-        const bool ok = c < nchunks;
+        const uint32_t so = (uint32_t)(kPfRowBytes * (c < nchunks ? c : nchunks - 1));
 #pragma unroll
-        for (int i = 0; i < NB; ++i)
-            ar[slot][i] = bld16(ra, (ok && aoff[i] != kOob) ? aoff[i] + (uint32_t)(kPfRowBytes * c) : kOob);
+        for (int i = 0; i < NB; ++i) ar[slot][i] = bld16s(ra, aoff[i], so);
     };
     // DIRECT: chunk c's four k-step operands sit in ring slot c % DD from
     // their load (issued when chunk c - DD finished with the slot) to the
@@ -308,9 +311,9 @@ __device__ __forceinline__ void pf_tile(const MoeGemmArgs& a, SH& sh, int e, int
     constexpr int DD = 4;
     u32x4 ad[DIRECT ? DD : 1][4];
     auto issue_ad = [&](int slot, int c) {
-        const bool ok = c < nchunks && aoff[0] != kOob;
+        const uint32_t so = (uint32_t)(kPfRowBytes * (c < nchunks ? c : nchunks - 1));
 #pragma unroll
-        for (int s4 = 0; s4 < 4; ++s4) ad[slot][s4] = bld16(ra, ok ? aoff[0] + (uint32_t)(kPfRowBytes * c + 16 * s4) : kOob);
+        for (int s4 = 0; s4 < 4; ++s4) ad[slot][s4] = bld16s(ra, aoff[0] + 16u * s4, so);
     };
     auto store_a = [&](int slot, int buf) {
 #pragma unroll
