@@ -14,8 +14,8 @@
 // route_align_kernel runs the routing of up to 64 tokens (route.hpp, one
 // wave per token) in the same workgroup and sorts straight from LDS, saving
 // a launch and a round trip of the ids through memory at decode sizes;
-// route_align_small_kernel does the same for up to 4 tokens and 64 pairs with
-// a one-wave sort.
+// route_align_small_kernel does the same for up to 32 tokens with a sort
+// that has no loop over pairs.
 #include "common.hpp"
 #include "launch.hpp"
 #include "route.hpp"
@@ -138,83 +138,90 @@ __global__ __launch_bounds__(kSortThreads) void route_align_kernel(
                     num_post_pad);
 }
 
-// Up to 4 tokens and 64 pairs: four waves route a token each while the
-// workgroup clears the LDS tables, then one wave sorts (a pair per lane)
-// without loops over pairs. A token routes to an expert at most once, so an expert's pairs are
-// a bitmask of tokens: the count is its popcount and a pair's rank within
-// the expert is the popcount of the lower tokens (pairs of one expert are in
-// token order, which is pair order). Padded segment starts come from one
-// wave scan over the experts (lane l owns experts VPL*l ..); sorted_ids and
-// block_expert are assembled in LDS and copied out with coalesced stores.
-// Same outputs as align_sort_body.
-constexpr int kSmallTokens = 4;
-constexpr int kSmallPairs = 64;
-constexpr int64_t kSmallCapMax = 4096;  // e.g. 64 pairs at block_m 64, 16 at 256
+// Up to 32 tokens: NW waves route the tokens (a token per wave at a time)
+// while the workgroup clears the LDS tables; then the sort has no loop over
+// pairs. A token routes to an expert at most once, so an expert's pairs are
+// a bitmask of tokens (LDS atomic OR): its count is a popcount and a pair's
+// rank within the expert the popcount of the lower tokens (pairs of one
+// expert are in token order, which is pair order). Padded segment starts
+// come from one wave scan over the experts (lane l owns experts VPL*l ..);
+// sorted_ids and block_expert are assembled in LDS and copied out with
+// coalesced stores. Same outputs as align_sort_body.
+constexpr int kSmallTokens = 32;        // token bitmasks are 32-bit
+constexpr int kSmallPairs = 512;
+constexpr int64_t kSmallCapMax = 4096;  // e.g. 480 pairs of 112 experts at block_m 32
 
-template <int VPL>
-__global__ __launch_bounds__(256) void route_align_small_kernel(
+template <int VPL, int NW>
+__global__ __launch_bounds__(NW * 64) void route_align_small_kernel(
     const float* __restrict__ logits, int T, int E, int topk, int renorm, int bm, int64_t cap,
     int32_t* __restrict__ ids, float* __restrict__ weights, int32_t* __restrict__ sorted_ids,
     int32_t* __restrict__ block_expert, int32_t* __restrict__ expert_offsets,
     int32_t* __restrict__ num_post_pad) {
+    constexpr int NT = NW * 64;
     __shared__ int32_t ids_lds[kSmallPairs];
     __shared__ uint32_t tokens[kMaxExperts];
     __shared__ int32_t start[kMaxExperts];
     __shared__ int32_t srt[kSmallCapMax];
     __shared__ int32_t blk[kSmallCapMax / 16];
-    const int wv = threadIdx.x >> 6;
-    const int lane = threadIdx.x & 63;
+    const int tid = threadIdx.x;
+    const int wv = tid >> 6;
+    const int lane = tid & 63;
     const int P = T * topk;
     const int ncap = (int)cap, nblk = (int)(cap / bm);
-    for (int i = threadIdx.x; i < E; i += 256) tokens[i] = 0u;
-    for (int i = threadIdx.x; i < ncap; i += 256) srt[i] = P;
-    for (int i = threadIdx.x; i < nblk; i += 256) blk[i] = -1;
-    for (int t = wv; t < T; t += 4)
+    for (int i = tid; i < E; i += NT) tokens[i] = 0u;
+    for (int i = tid; i < ncap; i += NT) srt[i] = P;
+    for (int i = tid; i < nblk; i += NT) blk[i] = -1;
+    for (int t = wv; t < T; t += NW)
         route_token<VPL>(logits + (int64_t)t * E, E, topk, renorm, ids + (int64_t)t * topk,
                          weights + (int64_t)t * topk, ids_lds + t * topk);
     __syncthreads();
-    if (wv != 0) return;
-    const int pe = lane < P ? ids_lds[lane] : -1;
-    const bool valid = (unsigned)pe < (unsigned)E;
-    const int pt = lane / topk;
-    if (valid) atomicOr(&tokens[pe], 1u << pt);
-    wave_lds_sync();
-    // Padded lengths of this lane's experts and their exclusive prefix.
-    int len[VPL], pad[VPL], local = 0;
-#pragma unroll
-    for (int c = 0; c < VPL; ++c) {
-        const int x = VPL * lane + c;
-        len[c] = x < E ? __popc(tokens[x]) : 0;
-        pad[c] = (len[c] + bm - 1) & -bm;  // block_m is a power of two
-        local += pad[c];
+    for (int p = tid; p < P; p += NT) {
+        const int e = ids_lds[p];
+        if ((unsigned)e < (unsigned)E) atomicOr(&tokens[e], 1u << (p / topk));
     }
-    int incl = local;
+    __syncthreads();
+    if (wv == 0) {
+        // Padded lengths of this lane's experts and their exclusive prefix.
+        int pad[VPL], local = 0;
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int o = __shfl_up(incl, off);
-        if (lane >= off) incl += o;
-    }
-    const int total = __shfl(incl, 63);
-    int base = incl - local;
-#pragma unroll
-    for (int c = 0; c < VPL; ++c) {
-        const int x = VPL * lane + c;
-        if (x < E) {
-            expert_offsets[x] = base;
-            start[x] = base;
-            for (int b = base / bm; b < (base + pad[c]) / bm; ++b) blk[b] = x;
+        for (int c = 0; c < VPL; ++c) {
+            const int x = VPL * lane + c;
+            const int len = x < E ? __popc(tokens[x]) : 0;
+            pad[c] = (len + bm - 1) & -bm;  // block_m is a power of two
+            local += pad[c];
         }
-        base += pad[c];
+        int incl = local;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const int o = __shfl_up(incl, off);
+            if (lane >= off) incl += o;
+        }
+        const int total = __shfl(incl, 63);
+        int base = incl - local;
+#pragma unroll
+        for (int c = 0; c < VPL; ++c) {
+            const int x = VPL * lane + c;
+            if (x < E) {
+                expert_offsets[x] = base;
+                start[x] = base;
+                for (int b = base / bm; b < (base + pad[c]) / bm; ++b) blk[b] = x;
+            }
+            base += pad[c];
+        }
+        if (lane == 0) {
+            expert_offsets[E] = total;
+            num_post_pad[0] = total;
+        }
     }
-    if (lane == 0) {
-        expert_offsets[E] = total;
-        num_post_pad[0] = total;
+    __syncthreads();
+    for (int p = tid; p < P; p += NT) {
+        const int e = ids_lds[p];
+        const int t = p / topk;
+        if ((unsigned)e < (unsigned)E) srt[start[e] + __popc(tokens[e] & ((1u << t) - 1u))] = p;
     }
-    wave_lds_sync();
-    if (valid) srt[start[pe] + __popc(tokens[pe] & ((1u << pt) - 1u))] = lane;
-    wave_lds_sync();
-    for (int i = lane; i < ncap; i += 64) sorted_ids[i] = srt[i];
-    for (int i = lane; i < nblk; i += 64) block_expert[i] = blk[i];
+    __syncthreads();
+    for (int i = tid; i < ncap; i += NT) sorted_ids[i] = srt[i];
+    for (int i = tid; i < nblk; i += NT) block_expert[i] = blk[i];
 }
 
 hipError_t launch_align_sort(const int32_t* ids, int P, int E, int bm, int64_t cap,
@@ -235,14 +242,19 @@ hipError_t launch_route_align(const float* logits, int T, int E, int topk, int r
                               hipStream_t s) {
     const dim3 grid(1), block(kSortThreads);
     const int vpl = (E + 63) / 64;
-#define MOE_LAUNCH_RA(V)                                                                                 \
-    do {                                                                                                 \
-        if (T <= kSmallTokens && T * topk <= kSmallPairs && cap <= kSmallCapMax)                         \
-            hipLaunchKernelGGL(route_align_small_kernel<V>, dim3(1), dim3(256), 0, s, logits, T, E, topk, \
-                               renorm, bm, cap, ids, weights, sorted_ids, block_expert, expert_offsets,  \
-                               num_post_pad);                                                            \
-        else                                                                                             \
-            hipLaunchKernelGGL(route_align_kernel<V>, grid, block, 0, s, logits, T, E, topk, renorm, bm, \
+    const bool small = T <= kSmallTokens && T * topk <= kSmallPairs && cap <= kSmallCapMax;
+#define MOE_LAUNCH_RA(V)                                                                                   \
+    do {                                                                                                   \
+        if (small && T <= 4)                                                                               \
+            hipLaunchKernelGGL((route_align_small_kernel<V, 4>), dim3(1), dim3(256), 0, s, logits, T, E,   \
+                               topk, renorm, bm, cap, ids, weights, sorted_ids, block_expert,             \
+                               expert_offsets, num_post_pad);                                              \
+        else if (small)                                                                                    \
+            hipLaunchKernelGGL((route_align_small_kernel<V, 16>), dim3(1), dim3(1024), 0, s, logits, T, E, \
+                               topk, renorm, bm, cap, ids, weights, sorted_ids, block_expert,             \
+                               expert_offsets, num_post_pad);                                              \
+        else                                                                                               \
+            hipLaunchKernelGGL(route_align_kernel<V>, grid, block, 0, s, logits, T, E, topk, renorm, bm,   \
                                cap, ids, weights, sorted_ids, block_expert, expert_offsets, num_post_pad); \
     } while (0)
     if (vpl <= 1) MOE_LAUNCH_RA(1);

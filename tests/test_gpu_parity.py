@@ -174,13 +174,16 @@ def test_route_align_matches_oracle(moe, name, bm):
 
 
 @pytest.mark.parametrize("T,E,topk", [(1, 1024, 16), (2, 8, 8), (4, 6, 4), (16, 8, 1), (1, 112, 15),
-                                      (16, 1024, 1), (1, 1024, 64), (4, 8, 8), (3, 20, 7), (4, 112, 15)])
+                                      (16, 1024, 1), (1, 1024, 64), (4, 8, 8), (3, 20, 7), (4, 112, 15),
+                                      (7, 112, 15), (32, 112, 15), (32, 1024, 16), (20, 8, 8),
+                                      (32, 6, 6), (33, 112, 15)])
 @pytest.mark.parametrize("bm", [16, 32, 256])
 def test_route_align_small_matches_oracle(moe, T, E, topk, bm):
-    """Small token counts: up to 16 pairs the fused call sorts with a single
-    wave (experts shared by several tokens, every expert chosen, E = 1024,
-    16 tokens, block_m up to 256), above that with the workgroup sort. The
-    whole capacity is compared (sentinel P and block -1 past the used part)."""
+    """Small token counts: up to 32 tokens (and 512 pairs, capacity 4096) the
+    fused call sorts with token bitmasks (experts shared by many tokens,
+    every expert chosen by every token, E = 1024, block_m up to 256); above
+    that, or with a larger capacity, with the workgroup sort. The whole
+    capacity is compared (sentinel P and block -1 past the used part)."""
     spec = synth.Spec("adhoc", T=T, H=256, I=128, E=E, topk=topk, seed=300 + T * E + topk)
     wl = synth.make(spec, with_weights=False)
     ids, w, s, be, off, npp = moe.moe_route_align(dev(wl.logits), topk, E, bm)
