@@ -18,8 +18,11 @@ on the launch stream around a graph of back-to-back launches cycling over the
 weight sets; its `traffic` is the HBM bytes per launch that rocprofv3 counters
 measured for the same kernel sources (profiles/traffic.json), else null.
 `stage_us` is an eager per-stage breakdown (events between launches, so it
-includes launch gaps). `cpu_baseline` is the CPU oracle on a bounded sample of
-the same workload.
+includes launch gaps). For the int4 workloads `requant` is the load-time
+MXFP4 -> int4-g32 conversion of one weight set (every expert of w13 and w2, 8
+experts per call into preallocated outputs): bytes read + written per pass
+over its duration, against HBM peak. `cpu_baseline` is the CPU oracle on a
+bounded sample of the same workload.
 """
 import argparse
 import json
@@ -93,6 +96,7 @@ class Layer:
                  torch.randint(0, 256, (E, H, I // 2), generator=g, device=dev, dtype=torch.uint8),
                  torch.randint(s.scale_lo, s.scale_hi + 1, (E, H, I // 32), generator=g, device=dev,
                                dtype=torch.uint8)]
+        self.mx = w if (int4 and host is not None) else None  # set 0 keeps its MXFP4 tensors
         if int4:
             q13, s13 = moe.requantize_mxfp4_experts(w[0], w[1])
             q2, s2 = moe.requantize_mxfp4_experts(w[2], w[3])
@@ -199,6 +203,41 @@ def weight_bytes_per_expert(H, I, fmt):
     w13 = 2 * I * (H // 2) + 2 * I * (H // 32) * sb
     w2 = H * (I // 2) + H * (I // 32) * sb
     return w13, w2
+
+
+def requant_rate(moe, mx, passes=5):
+    """Time the load-time requant of every expert of one weight set (w13 and
+    w2, 8 experts per call into preallocated outputs), HIP events on the
+    current stream. Free device memory is read before and after the timed
+    loop: the calls allocate nothing."""
+    import torch
+    outs = [(torch.empty_like(w), torch.empty(s.shape, dtype=torch.bfloat16, device=w.device))
+            for w, s in ((mx[0], mx[1]), (mx[2], mx[3]))]
+    pairs = [((mx[0], mx[1]), outs[0]), ((mx[2], mx[3]), outs[1])]
+    nbytes = sum(w.numel() + s.numel() + q.numel() + 2 * sb.numel() for (w, s), (q, sb) in pairs)
+
+    def one_pass():
+        calls = 0
+        for (w, s), (q, sb) in pairs:
+            for lo in range(0, w.shape[0], 8):
+                moe.mxfp4_to_int4g32_requant(w, s, lo, min(lo + 8, w.shape[0]), q, sb)
+                calls += 1
+        return calls
+    one_pass()
+    torch.cuda.synchronize()
+    free0 = torch.cuda.mem_get_info()[0]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(passes):
+        calls = one_pass()
+    e1.record()
+    e1.synchronize()
+    free1 = torch.cuda.mem_get_info()[0]
+    ms = e0.elapsed_time(e1) / passes
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    return {"bytes_per_pass": nbytes, "ms_per_pass": round(ms, 4), "achieved": round(gbps, 1),
+            "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "calls_per_pass": calls,
+            "experts_per_call": 8, "device_bytes_allocated_during_loop": free0 - free1}
 
 
 def cpu_baseline(wl, spec, seconds, fmt_name):
@@ -370,6 +409,8 @@ def main():
                      "down": round(stage_avg[2] * 1e3, 2), "combine": round(stage_avg[3] * 1e3, 2)},
         "roofline": roof,
     }
+    if int4:
+        line["requant"] = requant_rate(moe, layers[0].mx)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(host, spec, args.cpu_seconds,
                                             "int4_g32" if int4 else "MXFP4")

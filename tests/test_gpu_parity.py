@@ -436,6 +436,29 @@ def test_requant_partial_range_leaves_rest(moe):
     assert torch.all(qs[:3] == 7.0) and torch.all(qs[6:] == 7.0)
 
 
+def test_requant_chunked_allocates_nothing(moe):
+    """The 8-experts-per-call loop into preallocated outputs: no torch
+    allocation and no drop in free device memory across the calls (the
+    library has no scratch), and the result equals the oracle's bit for bit."""
+    wl = synth.small(T=1, H=512, I=256, E=20, topk=2, seed=12)
+    w, s = dev(wl.w13), dev(wl.w13_scale)
+    q = torch.empty_like(w)
+    qs = torch.empty(wl.w13_scale.shape, dtype=torch.bfloat16, device="cuda")
+    moe.mxfp4_to_int4g32_requant(w, s, 0, 1, q, qs)  # first call loads the code object
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    base_alloc = torch.cuda.memory_allocated()
+    free0 = torch.cuda.mem_get_info()[0]
+    for lo in range(0, w.shape[0], 8):
+        moe.mxfp4_to_int4g32_requant(w, s, lo, min(lo + 8, w.shape[0]), q, qs)
+    torch.cuda.synchronize()
+    assert torch.cuda.max_memory_allocated() == base_alloc
+    assert torch.cuda.mem_get_info()[0] == free0
+    rq, rs = oracle.requant_int4g32(wl.w13, wl.w13_scale)
+    assert np.array_equal(q.cpu().numpy(), rq)
+    assert np.array_equal(bf16_host(qs), rs)
+
+
 def test_int4_forward_tiny(moe):
     wl = synth.make(synth.specs()["tiny"])
     s = wl.spec
