@@ -526,12 +526,17 @@ def test_zero_tokens_is_noop(moe):
 
 # ------------------------------------------------------------- graph replay --
 
-def test_graph_replay_matches_eager(moe):
+@pytest.mark.parametrize("T,H,I,E,k,fused", [
+    (7, 512, 256, 16, 4, False),   # separate route and sort calls, wave-per-tile kernels
+    (1, 512, 1024, 16, 4, True),   # fused small routing, GEMV gate_up, persistent down
+    (8, 512, 256, 8, 4, True),     # single-wave MFMA tiles
+    (40, 512, 256, 8, 4, True),    # workgroup routing, 4-wave tiles with super-blocks
+])
+def test_graph_replay_matches_eager(moe, T, H, I, E, k, fused):
     """The whole layer captured in a HIP graph (no allocation or memset inside):
     several replays, with eager work and host synchronisation between them,
     each bit-identical to the eager result."""
-    wl = synth.small(T=7, H=512, I=256, E=16, topk=4, seed=77)
-    T, k, E, H, I = 7, 4, 16, 512, 256
+    wl = synth.small(T=T, H=H, I=I, E=E, topk=k, seed=77 + T)
     x, logits = x_dev(wl), dev(wl.logits)
     w13, w13s, w2, w2s = weights_dev(wl)
     bm = moe.moe_default_block_m(T, k, E)
@@ -546,8 +551,11 @@ def test_graph_replay_matches_eager(moe):
     ws = torch.empty(moe.moe_a16w4_workspace_size(T, H, I, E, k, bm), dtype=torch.uint8, device="cuda")
 
     def step():
-        moe.moe_route_topk(logits, k, True, ids, wts)
-        moe.moe_align_sort(ids, E, bm, out=srt)
+        if fused:
+            moe.moe_route_align(logits, k, E, bm, True, ids, wts, out=srt)
+        else:
+            moe.moe_route_topk(logits, k, True, ids, wts)
+            moe.moe_align_sort(ids, E, bm, out=srt)
         moe.moe_a16w4_forward(x, w13, w13s, w2, w2s, ids, wts, srt[0], srt[1], srt[3], bm, out=out,
                               workspace=ws)
 
