@@ -48,9 +48,19 @@ __device__ void align_sort_body(SortShared& sh, const int32_t* ids, int P, int E
         sh.running[e] = 0;
     }
     __syncthreads();
-    for (int p = tid; p < P; p += kSortThreads) {
-        const int e = ids[p];
-        if ((unsigned)e < (unsigned)E) atomicAdd(&sh.counts[e], 1);
+    // Eight ids per thread in flight (clamped index, no branch), then the
+    // counts: one memory round trip per 8192 pairs instead of per 1024.
+    for (int base = 0; base < P; base += 8 * kSortThreads) {
+        int ev[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int p = base + u * kSortThreads + tid;
+            ev[u] = ids[p < P ? p : P - 1];
+            if (p >= P) ev[u] = -1;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if ((unsigned)ev[u] < (unsigned)E) atomicAdd(&sh.counts[ev[u]], 1);
     }
     __syncthreads();
 
@@ -88,12 +98,16 @@ __device__ void align_sort_body(SortShared& sh, const int32_t* ids, int P, int E
     for (int64_t r = total + tid; r < cap; r += kSortThreads) sorted_ids[r] = P;
     for (int64_t b = total / bm + tid; b < cap / bm; b += kSortThreads) block_expert[b] = -1;
 
-    // Stable scatter, 1024 pairs per tile.
+    // Stable scatter, 1024 pairs per tile; the next tile's id is loaded
+    // while this one is placed.
+    int e_next = P > 0 ? ids[tid < P ? tid : P - 1] : -1;
     for (int base = 0; base < P; base += kSortThreads) {
+        const int p = base + tid;
+        const int e = p < P ? e_next : -1;
+        const int pn = p + kSortThreads;
+        e_next = pn < P ? ids[pn] : -1;
         for (int i = tid; i < kSortWaves * E; i += kSortThreads) sh.masks[i] = 0ull;
         __syncthreads();
-        const int p = base + tid;
-        const int e = p < P ? ids[p] : -1;
         const bool valid = (unsigned)e < (unsigned)E;
         if (valid) atomicOr(&sh.masks[wv * E + e], 1ull << lane);
         __syncthreads();
