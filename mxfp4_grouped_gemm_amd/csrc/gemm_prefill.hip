@@ -56,9 +56,11 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int kPfWRows = 64;
 constexpr int kPfStage = 4;  // chunks per weight stage
 // Single-wave tiles up to this many tokens (at most one 32-row block per
-// expert needs T <= 32; above 16 tokens blocks fill up and the 4-wave tiles,
-// which share each activation chunk between four waves, are faster).
-constexpr int kPfDirectMaxTokens = 16;
+// expert needs T <= 32). For gate_up, above 16 tokens the blocks fill up and
+// the 4-wave tiles, which share each activation chunk between four waves,
+// are faster; for down the single-wave tiles stay ahead up to 32.
+constexpr int kPfDirectMaxTokens1 = 16;
+constexpr int kPfDirectMaxTokens2 = 32;
 template <int NBMAX>
 struct __attribute__((aligned(16))) PfShared {
     uint8_t a[kPfABufs][NBMAX * kPfBlockRows * kPfRowBytes];
@@ -599,7 +601,7 @@ int64_t prefill_list_bytes(int64_t cap) { return (cap / kPfBlockRows + 1) * 16 +
 hipError_t launch_prefill(const MoeGemmArgs& a, int stage, void* list_ws, hipStream_t s) {
     int4* list = (int4*)list_ws;
     const int64_t nblocks = a.cap / kPfBlockRows;
-    if (a.T <= kPfDirectMaxTokens) {
+    if (a.T <= (stage == 1 ? kPfDirectMaxTokens1 : kPfDirectMaxTokens2)) {
         const int ntiles = stage == 1 ? a.I / 32 : a.H / 64;
         const dim3 grid((unsigned)(8 * ((nblocks + 7) / 8) * ntiles)), block(64);
         if (a.fmt == kFmtMxfp4) {

@@ -293,7 +293,7 @@ def test_forward_prefill_path(moe, T, H, I, E, topk, hot):
     (13, 768, 256, 4, 3, 0, 0),    # ragged T
     (16, 512, 256, 12, 3, 3, 0),   # skewed: hot experts hold every token
     (16, 512, 512, 8, 4, 0, 1),    # int4-g32 weights
-    (32, 512, 256, 12, 3, 3, 0),   # 17..32 tokens: the 4-wave tiles, 2-block super-blocks
+    (32, 512, 256, 12, 3, 3, 0),   # 17..32 tokens: 4-wave gate_up tiles, single-wave down tiles
 ])
 def test_forward_direct_tiles(moe, T, H, I, E, topk, hot, fmt):
     """Batches of 5..16 tokens (at least 32 pairs, 32-row blocks) take
