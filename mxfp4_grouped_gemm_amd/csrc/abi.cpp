@@ -76,7 +76,7 @@ int64_t moe_align_sort_capacity(int T, int topk, int E, int block_m) {
 int moe_default_block_m(int T, int topk, int E) {
     (void)topk;
     (void)E;
-    if (T <= 4) return 16;
+    if (T <= 8) return 16;
     return 32;
 }
 

@@ -285,7 +285,7 @@ __global__ __launch_bounds__(kGemvWaves2 * 64) void stage2_gemv_tok_kernel(MoeGe
 // in flight instead of draining between short workgroups. Router-weighted
 // row sums go to LDS; after one barrier the rows are summed over the slots
 // in ascending j, the combine's order.
-constexpr int kRowsMax = 64;   // rows per workgroup (bounds the LDS sums)
+constexpr int kRowsMax = 128;  // rows per workgroup (bounds the LDS sums)
 constexpr int kSlotsMax = 16;  // waves per workgroup = top-k
 
 // Four weight rows in half-block units: lane l holds half-block 64c + l
@@ -404,16 +404,16 @@ __global__ __launch_bounds__(kSlotsMax * 64) void stage2_gemv_rows_kernel(MoeGem
         consume(WB, lds_scale[j][1], s + 1);
     }
     __syncthreads();
-    if ((int)threadIdx.x < nrows) {
+    for (int r = (int)threadIdx.x; r < nrows; r += (int)blockDim.x) {  // nrows may exceed the threads
         float sum = 0.f;
-        for (int jj = 0; jj < a.topk; ++jj) sum += red[jj][threadIdx.x];
-        a.out[(int64_t)t * H + row0 + threadIdx.x] = f32_to_bf16_bits(sum);
+        for (int jj = 0; jj < a.topk; ++jj) sum += red[jj][r];
+        a.out[(int64_t)t * H + row0 + r] = f32_to_bf16_bits(sum);
     }
 }
 
 bool gemv_eligible(const MoeGemmArgs& a) {
     const int max_rows = a.T < a.bm ? a.T : a.bm;
-    return a.fmt == kFmtMxfp4 && max_rows <= 4 && a.topk <= kGemvWaves2 * kSlotsPerWave &&
+    return a.fmt == kFmtMxfp4 && max_rows <= 8 && a.topk <= kGemvWaves2 * kSlotsPerWave &&
            a.H <= 4096 && a.I <= 4096 && a.H % 512 == 0 && a.I % 512 == 0 &&
            (int64_t)a.T * a.topk * a.I * 2 < 0x7fff0000LL;
 }
@@ -432,7 +432,8 @@ hipError_t launch_gemv_stage(const MoeGemmArgs& a, int stage, hipStream_t s) {
         const int rows = a.T < a.bm ? a.T : a.bm;
         if (rows <= 1) launch_stage1_nr<1>(a, nch, s);
         else if (rows <= 2) launch_stage1_nr<2>(a, nch, s);
-        else launch_stage1_nr<4>(a, nch, s);
+        else if (rows <= 4) launch_stage1_nr<4>(a, nch, s);
+        else launch_stage1_nr<8>(a, nch, s);
     } else {
         const int nhc = (a.I / 16 + 63) / 64;
         if (nhc > 3) {

@@ -252,9 +252,13 @@ def test_forward_ragged_shapes(moe, T, H, I, E, topk, bm):
     (3, 6, 4, 512, 3072),    # three chunks; runs of 7 down rows end in a partial 4-row step
     (4, 16, 16, 512, 3072),  # 16 slots: one wave per slot, 1024 threads
     (1, 6, 4, 512, 4096),    # I above 3072: the 8-wave down kernel
+    (7, 16, 4, 512, 1024),   # 5..8 tokens: rows reloaded in sequence up to 8 per block
+    (8, 8, 8, 512, 2048),    # topk == E: every block holds all 8 tokens
+    (6, 12, 6, 1024, 1536),
+    (8, 4, 1, 512, 1024),    # topk 1: one wave per workgroup sums up to 128 down rows
 ])
 def test_forward_gemv_path_small(moe, T, E, topk, H, I):
-    """Decode blocks of at most 4 token rows with K a multiple of 512 take the
+    """Decode blocks of at most 8 token rows with K a multiple of 512 take the
     GEMV-shaped kernels; H=512 keeps the oracle fast."""
     wl = synth.small(T=T, H=H, I=I, E=E, topk=topk, seed=40 + T + I)
     out = run_layer(moe, wl, topk)
@@ -296,19 +300,18 @@ def test_forward_prefill_path(moe, T, H, I, E, topk, hot):
     (32, 512, 256, 12, 3, 3, 0),   # 17..32 tokens: 4-wave gate_up tiles, single-wave down tiles
 ])
 def test_forward_direct_tiles(moe, T, H, I, E, topk, hot, fmt):
-    """Batches of 5..16 tokens (at least 32 pairs, 32-row blocks) take
-    single-wave MFMA tiles, one per (block, 64 weight rows); every token is
-    compared."""
+    """Batches of up to 16 tokens sorted into 32-row blocks (at least 32
+    pairs) take single-wave MFMA tiles, one per (block, 64 weight rows);
+    every token is compared. (32-row blocks are the default above 8 tokens.)"""
     wl = synth.small(T=T, H=H, I=I, E=E, topk=topk, seed=11 * T + E + fmt, hot=hot)
-    assert moe.moe_default_block_m(T, topk, E) == 32
     ids, w = oracle.route_topk(wl.logits, topk)
     if fmt == 0:
-        out = run_layer(moe, wl, topk)
+        out = run_layer(moe, wl, topk, bm=32)
         ref = oracle.moe_forward(wl.x, wl.w13, wl.w13_scale, wl.w2, wl.w2_scale, 0, ids, w, I=I)
     else:
         q13, s13 = moe.requantize_mxfp4_experts(dev(wl.w13), dev(wl.w13_scale))
         q2, s2 = moe.requantize_mxfp4_experts(dev(wl.w2), dev(wl.w2_scale))
-        out = run_layer(moe, wl, topk, fmt=1, w=(q13, s13, q2, s2))
+        out = run_layer(moe, wl, topk, fmt=1, w=(q13, s13, q2, s2), bm=32)
         rq13, rs13 = oracle.requant_int4g32(wl.w13, wl.w13_scale)
         rq2, rs2 = oracle.requant_int4g32(wl.w2, wl.w2_scale)
         ref = oracle.moe_forward(wl.x, rq13, rs13, rq2, rs2, 1, ids, w, I=I)
