@@ -239,7 +239,7 @@ moe_status moe_a16w4_forward_stages(const uint16_t* x, const uint8_t* w13, const
     a.out = out;
     hipStream_t s = (hipStream_t)stream;
     moe_status st = MOE_OK;
-    // Kernel family per shape: GEMV waves for blocks of <= 4 token rows,
+    // Kernel family per shape: GEMV waves for blocks of <= 8 token rows,
     // the LDS-tiled MFMA kernels at prefill sizes, wave-per-tile MFMA
     // kernels for other 16/32-row blocks, split-K workgroups for 64.
     const bool decode = block_m <= 32;

@@ -1,4 +1,4 @@
-// GEMV-shaped decode kernels for expert blocks of at most 4 token rows
+// GEMV-shaped decode kernels for expert blocks of at most 8 token rows
 // (MXFP4 weights, K a multiple of 512 up to 4096).
 //
 // With one or a few activation rows per expert block, 15/16 of every MFMA
@@ -15,7 +15,7 @@
 //    accumulates v_dot2_f32_bf16 against the matching 32 activations; row
 //    sums meet with permlane32/16 swaps and DPP row rotations.
 //
-// Stage 1 is block-major (one expert block, its <= 4 rows share the weight
+// Stage 1 is block-major (one expert block, its <= 8 rows share the weight
 // stream) and stores h by pair index. Stage 2 is token-major: a workgroup
 // owns (token, a run of output rows) with one wave per top-k slot (expert of
 // slot j from topk_ids); each wave scales its row sums by the router weight
