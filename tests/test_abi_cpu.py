@@ -19,9 +19,9 @@ HEADER = os.path.join(ROOT, "include", "moe_a16w4.h")
 
 @pytest.fixture(scope="module")
 def moe():
-    from mxfp4_grouped_gemm_amd import build as b
-    if not os.path.exists(b.LIB):
-        b.build()
+    if not os.path.exists(os.path.join(ROOT, "mxfp4_grouped_gemm_amd", "libmoe_a16w4.so")):
+        import __graft_entry__
+        __graft_entry__.build()
     import mxfp4_grouped_gemm_amd as m
     return m
 
