@@ -187,7 +187,7 @@ def stage1_kernel_name(T, bm, fmt, H, I, topk, E):
     """Which gate_up kernel the library launches for this shape (the rule of
     gemv_eligible / forward_stages in the C sources, restated for the label)."""
     rows = min(T, bm)
-    if (bm <= 32 and fmt == 0 and rows <= 8 and topk <= 16 and H <= 4096 and I <= 4096
+    if (bm <= 32 and fmt == 0 and rows <= 8 and H <= 4096 and I <= 4096
             and H % 512 == 0 and I % 512 == 0):
         return "stage1_gemv_kernel"
     P = T * topk

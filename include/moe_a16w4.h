@@ -161,10 +161,7 @@ moe_status moe_a16w4_forward(const uint16_t* x, const uint8_t* w13, const void* 
  * the previous stage wrote into the same workspace for the same arguments.
  * moe_a16w4_forward == moe_a16w4_forward_stages with MOE_STAGE_ALL. Same
  * arguments, requirements and errors as moe_a16w4_forward; stages == 0 or
- * unknown bits give MOE_ERR_INVALID_ARG. For decode shapes (MXFP4, at most 4
- * token rows per expert block, H and I multiples of 512 up to 4096,
- * topk <= 16) the DOWN launch also performs the combine and writes out;
- * MOE_STAGE_COMBINE then enqueues nothing. */
+ * unknown bits give MOE_ERR_INVALID_ARG. */
 #define MOE_STAGE_GATE_UP 1u
 #define MOE_STAGE_DOWN 2u
 #define MOE_STAGE_COMBINE 4u

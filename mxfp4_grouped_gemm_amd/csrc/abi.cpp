@@ -246,8 +246,6 @@ moe_status moe_a16w4_forward_stages(const uint16_t* x, const uint8_t* w13, const
     const bool gemv = decode && moe::gemv_eligible(a);
     const bool prefill = !gemv && moe::prefill_eligible(a) && P >= moe::kPrefillMinPairs;
     void* list = (char*)workspace + L.list_off;
-    // The GEMV decode path combines inside its down launch.
-    const bool combined_in_down = gemv;
     if (stages & MOE_STAGE_GATE_UP) {
         st = hip_status(prefill ? moe::launch_prefill(a, 1, list, s)
                         : decode ? moe::launch_decode_stage(a, 1, s) : moe::launch_stage1(a, s),
@@ -260,7 +258,7 @@ moe_status moe_a16w4_forward_stages(const uint16_t* x, const uint8_t* w13, const
                         "moe_a16w4_forward (down)");
         if (st != MOE_OK) return st;
     }
-    if ((stages & MOE_STAGE_COMBINE) && !combined_in_down)
+    if (stages & MOE_STAGE_COMBINE)
         st = hip_status(moe::launch_combine(a.y, topk_ids, topk_weights, T, H, E, topk, out, s),
                         "moe_a16w4_forward (combine)");
     return st;

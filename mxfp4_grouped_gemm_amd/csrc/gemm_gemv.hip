@@ -15,20 +15,18 @@
 //    accumulates v_dot2_f32_bf16 against the matching 32 activations; row
 //    sums meet with permlane32/16 swaps and DPP row rotations.
 //
-// Stage 1 is block-major (one expert block, its <= 8 rows share the weight
-// stream) and stores h by pair index. Stage 2 is token-major: a workgroup
-// owns (token, a run of output rows) with one wave per top-k slot (expert of
-// slot j from topk_ids); each wave scales its row sums by the router weight
-// and the slots meet in LDS in a fixed order, so the weighted combine
-// happens in the same launch and no per-pair output is stored.
+// Both stages are block-major (one expert block; its <= 8 token rows share
+// the weight stream, dotted one after another against the same registers).
+// Stage 1 stores h by pair index, stage 2 stores fp32 y by pair index, and
+// the combine kernel sums the slots of each token.
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace moe {
 
-constexpr int kGemvWaves1 = 4;  // stage 1: waves per workgroup (independent tiles)
-constexpr int kGemvWaves2 = 8;  // stage 2: waves per workgroup (slots of one token)
-constexpr int kSlotsPerWave = 2;
+constexpr int kGemvWaves1 = 4;            // stage 1: waves per workgroup (independent tiles)
+constexpr int kDownWaves = 4;             // stage 2: waves per workgroup
+constexpr int kDownRows = 4 * kDownWaves; // stage 2: output rows per workgroup
 
 template <int CTRL>
 __device__ __forceinline__ float ror_add(float v) {
@@ -90,13 +88,13 @@ struct GemvWeights {
             so = (uint32_t)rows.first0 * nblk + 16u * lane;
         else if (lane < ptot)
             so = (uint32_t)rows.first1 * nblk + 16u * (lane - p0);
-        sc = bld16(rs, so);
+        sc = bld16nt(rs, so);
 #pragma unroll
         for (int r = 0; r < 4; ++r)
 #pragma unroll
             for (int c = 0; c < NCH; ++c) {
                 const int blk = 64 * c + lane;
-                w[r][c] = bld16(rw, blk < nblk ? (uint32_t)rows.row(r) * (uint32_t)(nblk * 16) + 16u * blk : kOob);
+                w[r][c] = bld16nt(rw, blk < nblk ? (uint32_t)rows.row(r) * (uint32_t)(nblk * 16) + 16u * blk : kOob);
             }
     }
     // Scale bytes into wave-private LDS: row slot r at [r * nblk, +nblk).
@@ -152,8 +150,13 @@ __device__ __forceinline__ void gemv_dot(const GemvWeights<NCH>& W, const uint8_
 // The activations of the first NR rows are loaded with the weights; further
 // rows (rare at decode sizes) reuse those registers one row at a time, so
 // the register footprint -- and the occupancy -- is that of NR rows.
+// One token row per block (T = 1) fits 79 VGPRs without spilling: six waves
+// per SIMD keep about 1.5x more weight bytes in flight per CU than the
+// compiler's default of four (35 -> 32 us at the production decode shape).
+// With rows reloaded in sequence the default allocation is faster.
 template <int NR, int NRMAX, int NCH>
-__global__ __launch_bounds__(kGemvWaves1 * 64) void stage1_gemv_kernel(MoeGemmArgs a) {
+__global__ __launch_bounds__(kGemvWaves1 * 64) __attribute__((amdgpu_waves_per_eu(NRMAX == 1 ? 6 : 1)))
+void stage1_gemv_kernel(MoeGemmArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t lds_scale[kGemvWaves1][4 * 64 * NCH];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar addressing
@@ -209,85 +212,6 @@ __global__ __launch_bounds__(kGemvWaves1 * 64) void stage1_gemv_kernel(MoeGemmAr
     }
 }
 
-// Stage 2 + combine: workgroup = (token t, output columns n0..n0+3); wave w
-// takes slots j = w + 8 s (s < kSlotsPerWave) of the token.
-template <int NCH>
-__global__ __launch_bounds__(kGemvWaves2 * 64) void stage2_gemv_tok_kernel(MoeGemmArgs a) {
-    __shared__ __attribute__((aligned(16))) uint8_t lds_scale[kGemvWaves2][kSlotsPerWave][4 * 64 * NCH];
-    __shared__ float red[kGemvWaves2][4];
-    const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar addressing
-    const int cpt = a.H / 4;
-    const int t = (int)(blockIdx.x / cpt);
-    const int n0 = (int)(blockIdx.x % cpt) * 4;
-    const int H = a.H, I = a.I, nblk = I / 32;
-    const int topk = a.topk;
-
-    // One round trip: the slots' experts and router weights.
-    int e[kSlotsPerWave];
-    float wt[kSlotsPerWave];
-    bool ok[kSlotsPerWave];
-#pragma unroll
-    for (int s = 0; s < kSlotsPerWave; ++s) {
-        const int j = wave + kGemvWaves2 * s;
-        const int64_t p = (int64_t)t * topk + j;
-        e[s] = j < topk ? a.topk_ids[p] : -1;
-        ok[s] = (unsigned)e[s] < (unsigned)a.E;
-        wt[s] = ok[s] ? a.topk_weights[p] : 0.0f;
-    }
-    const rsrc_t rx = make_rsrc(a.h, (uint32_t)((int64_t)a.T * topk * I * 2));
-    u32x4 x[kSlotsPerWave][NCH][4];
-#pragma unroll
-    for (int s = 0; s < kSlotsPerWave; ++s) {
-        const int64_t p = (int64_t)t * topk + wave + kGemvWaves2 * s;
-        issue_x<NCH>(x[s], rx, ok[s] ? (uint32_t)p * (uint32_t)(2 * I) : kOob, nblk, lane);
-    }
-    GemvWeights<NCH> W[kSlotsPerWave];
-#pragma unroll
-    for (int s = 0; s < kSlotsPerWave; ++s) {
-        const int es = ok[s] ? e[s] : 0;
-        const rsrc_t rw = make_rsrc(a.w2 + (int64_t)es * H * (I / 2), ok[s] ? (uint32_t)((int64_t)H * (I / 2)) : 0u);
-        const rsrc_t rs = make_rsrc((const uint8_t*)a.w2_scale + (int64_t)es * H * nblk,
-                                    ok[s] ? (uint32_t)((int64_t)H * nblk) : 0u);
-        W[s].issue(rw, rs, GemvRows{n0, 4, 0}, nblk, lane);
-    }
-#pragma unroll
-    for (int s = 0; s < kSlotsPerWave; ++s) W[s].stage_scales(lds_scale[wave][s], nblk, lane);
-    wave_lds_sync();
-
-    float v[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int s = 0; s < kSlotsPerWave; ++s) {
-        if (!ok[s]) continue;  // uniform: the slot's expert is the same for the whole wave
-        float acc[4] = {0.f, 0.f, 0.f, 0.f};
-        gemv_dot<NCH>(W[s], lds_scale[wave][s], x[s], nblk, lane, acc);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = fmaf(wt[s], acc[r], v[r]);
-    }
-    // Rows after reduce4: columns n0 + (0, 2, 1, 3) in 16-lane rows 0..3.
-    const float q = reduce4(v);
-    const int rho = lane >> 4;
-    if ((lane & 15) == 0) red[wave][(rho == 1) ? 2 : (rho == 2) ? 1 : rho] = q;
-    __syncthreads();
-    if (threadIdx.x < 4) {
-        float sum = 0.f;
-#pragma unroll
-        for (int w = 0; w < kGemvWaves2; ++w) sum += red[w][threadIdx.x];
-        a.out[(int64_t)t * H + n0 + threadIdx.x] = f32_to_bf16_bits(sum);
-    }
-}
-
-// Stage 2 + combine, persistent over a run of output rows: workgroup =
-// (token t, rows [row0, row0 + nrows)), one wave per top-k slot j. The wave
-// keeps its pair's h row in registers for the whole run and streams its
-// expert's down rows four at a time, the next four in flight while the
-// current ones are dotted, so every CU keeps a steady stream of weight loads
-// in flight instead of draining between short workgroups. Router-weighted
-// row sums go to LDS; after one barrier the rows are summed over the slots
-// in ascending j, the combine's order.
-constexpr int kRowsMax = 128;  // rows per workgroup (bounds the LDS sums)
-constexpr int kSlotsMax = 16;  // waves per workgroup = top-k
-
 // Four weight rows in half-block units: lane l holds half-block 64c + l
 // (16 K elements, 8 code bytes) of each row, so K = 16 * nhb fills the lanes
 // evenly whenever nhb is a multiple of 64 (I = 3072: three chunks, no idle
@@ -300,13 +224,13 @@ struct HalfRows {
 
     __device__ __forceinline__ void issue_run(rsrc_t rw, rsrc_t rs, int first, int nv, int nhb, int lane) {
         const int nblk = nhb / 2, ptot = nv * nblk / 16;
-        sc = bld16(rs, lane < ptot ? (uint32_t)first * nblk + 16u * lane : kOob);
+        sc = bld16nt(rs, lane < ptot ? (uint32_t)first * nblk + 16u * lane : kOob);
 #pragma unroll
         for (int r = 0; r < 4; ++r)
 #pragma unroll
             for (int c = 0; c < NHC; ++c) {
                 const int hb = 64 * c + lane;
-                w[r][c] = bld8(rw, (r < nv && hb < nhb) ? (uint32_t)(first + r) * (uint32_t)(nhb * 8) + 8u * hb
+                w[r][c] = bld8nt(rw, (r < nv && hb < nhb) ? (uint32_t)(first + r) * (uint32_t)(nhb * 8) + 8u * hb
                                                         : kOob);
             }
     }
@@ -354,66 +278,59 @@ __device__ __forceinline__ void half_dot(const HalfRows<NHC>& W, const uint8_t* 
     }
 }
 
-template <int NHC>
-__global__ __launch_bounds__(kSlotsMax * 64) void stage2_gemv_rows_kernel(MoeGemmArgs a, int G, int R) {
-    __shared__ __attribute__((aligned(16))) uint8_t lds_scale[kSlotsMax][2][4 * 32 * NHC];
-    __shared__ float red[kSlotsMax][kRowsMax];
+// Stage 2, block-major like stage 1: unit = (expert block b, output rows
+// n0..n0+3); a wave reads those 4 rows of the block's expert once (6 KB at
+// I = 3072, one memory round trip in half-block loads) and dots them with the
+// block's <= NRMAX h rows one after another, storing fp32 y[pair][n]; the
+// combine kernel follows. A workgroup covers kDownRows consecutive rows of one
+// block, so its loads are one contiguous run of the expert's rows.
+template <int NHC, int NRMAX>
+__global__ __launch_bounds__(kDownWaves * 64) void stage2_gemv_blk_kernel(MoeGemmArgs a) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds_scale[kDownWaves][4 * 32 * NHC];
     const int lane = threadIdx.x & 63;
-    const int j = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    // Workgroups of one row run (all tokens) are consecutive in L and land
-    // on one XCD, so tokens routed to the same expert share its rows in L2.
-    const int nbp = (int)gridDim.x;  // a multiple of 8
-    const int L = (int)(blockIdx.x % 8) * (nbp / 8) + (int)(blockIdx.x / 8);
-    if (L >= a.T * G) return;
-    const int g = L / a.T, t = L % a.T;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar addressing
     const int H = a.H, I = a.I, nblk = I / 32, nhb = I / 16;
-    const int row0 = g * R;
-    const int nrows = min(R, H - row0);
-    const int nsteps = (nrows + 3) / 4;
-
-    const int64_t p = (int64_t)t * a.topk + j;
-    const int e = a.topk_ids[p];
-    const bool ok = (unsigned)e < (unsigned)a.E;
-    const float wt = ok ? a.topk_weights[p] : 0.0f;
-    const int es = ok ? e : 0;
-    const rsrc_t rx = make_rsrc(a.h, (uint32_t)((int64_t)a.T * a.topk * I * 2));
-    const rsrc_t rw = make_rsrc(a.w2 + (int64_t)es * H * (I / 2), ok ? (uint32_t)((int64_t)H * (I / 2)) : 0u);
-    const rsrc_t rs = make_rsrc((const uint8_t*)a.w2_scale + (int64_t)es * H * nblk,
-                                ok ? (uint32_t)((int64_t)H * nblk) : 0u);
-    u32x4 x[NHC][2];
-    issue_xh<NHC>(x, rx, ok ? (uint32_t)p * (uint32_t)(2 * I) : kOob, nhb, lane);
-
-    auto consume = [&](const HalfRows<NHC>& W, uint8_t* lsc, int s) {
-        W.stage_scales(lsc, nhb, lane);
-        wave_lds_sync();
-        float acc[4] = {0.f, 0.f, 0.f, 0.f};
-        half_dot<NHC>(W, lsc, x, nhb, lane, acc);
-        // Rows after reduce4: 4s + (0, 2, 1, 3) in 16-lane rows 0..3.
-        const float q = reduce4(acc);
-        const int rho = lane >> 4;
-        const int r = 4 * s + ((rho == 1) ? 2 : (rho == 2) ? 1 : rho);
-        if ((lane & 15) == 0 && r < nrows) red[j][r] = wt * q;
-    };
-    HalfRows<NHC> WA, WB;
-    WA.issue_run(rw, rs, row0, min(4, nrows), nhb, lane);
-    for (int s = 0; s < nsteps; s += 2) {
-        if (s + 1 < nsteps) WB.issue_run(rw, rs, row0 + 4 * (s + 1), min(4, nrows - 4 * (s + 1)), nhb, lane);
-        consume(WA, lds_scale[j][0], s);
-        if (s + 1 >= nsteps) break;
-        if (s + 2 < nsteps) WA.issue_run(rw, rs, row0 + 4 * (s + 2), min(4, nrows - 4 * (s + 2)), nhb, lane);
-        consume(WB, lds_scale[j][1], s + 1);
+    const int gpb = H / kDownRows;  // row groups per block
+    const int64_t b = blockIdx.x / gpb;
+    const int g = (int)(blockIdx.x % gpb);
+    const int nused = *a.num_post_pad / a.bm;  // blocks holding pairs
+    if (b >= nused) return;
+    const int64_t row0 = b * a.bm;
+    const int e = a.block_expert[b];
+    const int P = a.T * a.topk;
+    int pair[NRMAX], nvalid = 0;
+#pragma unroll
+    for (int m = 0; m < NRMAX; ++m) {
+        pair[m] = a.sorted_ids[row0 + m];
+        nvalid += (pair[m] >= 0 && pair[m] < P) ? 1 : 0;
     }
-    __syncthreads();
-    for (int r = (int)threadIdx.x; r < nrows; r += (int)blockDim.x) {  // nrows may exceed the threads
-        float sum = 0.f;
-        for (int jj = 0; jj < a.topk; ++jj) sum += red[jj][r];
-        a.out[(int64_t)t * H + row0 + r] = f32_to_bf16_bits(sum);
+    const int n0 = g * kDownRows + 4 * wave;
+    if ((unsigned)e >= (unsigned)a.E) return;
+    const rsrc_t rw = make_rsrc(a.w2 + (int64_t)e * H * (I / 2), (uint32_t)((int64_t)H * (I / 2)));
+    const rsrc_t rs = make_rsrc((const uint8_t*)a.w2_scale + (int64_t)e * H * nblk, (uint32_t)((int64_t)H * nblk));
+    const rsrc_t rx = make_rsrc(a.h, (uint32_t)((int64_t)P * I * 2));
+    u32x4 x[NHC][2];
+    issue_xh<NHC>(x, rx, nvalid > 0 ? (uint32_t)pair[0] * (uint32_t)(2 * I) : kOob, nhb, lane);
+    HalfRows<NHC> W;
+    W.issue_run(rw, rs, n0, 4, nhb, lane);
+    W.stage_scales(lds_scale[wave], nhb, lane);
+    wave_lds_sync();
+    const int rho = lane >> 4;
+    const int r = (rho == 1) ? 2 : (rho == 2) ? 1 : rho;  // rows after reduce4: (0, 2, 1, 3)
+#pragma unroll
+    for (int m = 0; m < NRMAX; ++m) {
+        if (m >= nvalid) break;
+        if (m > 0) issue_xh<NHC>(x, rx, (uint32_t)pair[m] * (uint32_t)(2 * I), nhb, lane);
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+        half_dot<NHC>(W, lds_scale[wave], x, nhb, lane, acc);
+        const float q = reduce4(acc);
+        if ((lane & 15) == 0) a.y[(int64_t)pair[m] * H + n0 + r] = q;
     }
 }
 
 bool gemv_eligible(const MoeGemmArgs& a) {
     const int max_rows = a.T < a.bm ? a.T : a.bm;
-    return a.fmt == kFmtMxfp4 && max_rows <= 8 && a.topk <= kGemvWaves2 * kSlotsPerWave &&
+    return a.fmt == kFmtMxfp4 && max_rows <= 8 &&
            a.H <= 4096 && a.I <= 4096 && a.H % 512 == 0 && a.I % 512 == 0 &&
            (int64_t)a.T * a.topk * a.I * 2 < 0x7fff0000LL;
 }
@@ -426,6 +343,15 @@ static void launch_stage1_nr(const MoeGemmArgs& a, int nch, hipStream_t s) {
     else hipLaunchKernelGGL((stage1_gemv_kernel<1, NRMAX, 2>), grid, block, 0, s, a);
 }
 
+template <int NHC>
+static void launch_down_blk(const MoeGemmArgs& a, int rows, hipStream_t s) {
+    const dim3 grid((unsigned)((a.cap / a.bm) * (a.H / kDownRows))), block(kDownWaves * 64);
+    if (rows <= 1) hipLaunchKernelGGL((stage2_gemv_blk_kernel<NHC, 1>), grid, block, 0, s, a);
+    else if (rows <= 2) hipLaunchKernelGGL((stage2_gemv_blk_kernel<NHC, 2>), grid, block, 0, s, a);
+    else if (rows <= 4) hipLaunchKernelGGL((stage2_gemv_blk_kernel<NHC, 4>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((stage2_gemv_blk_kernel<NHC, 8>), grid, block, 0, s, a);
+}
+
 hipError_t launch_gemv_stage(const MoeGemmArgs& a, int stage, hipStream_t s) {
     if (stage == 1) {
         const int nch = (a.H / 32 + 63) / 64;
@@ -436,24 +362,11 @@ hipError_t launch_gemv_stage(const MoeGemmArgs& a, int stage, hipStream_t s) {
         else launch_stage1_nr<8>(a, nch, s);
     } else {
         const int nhc = (a.I / 16 + 63) / 64;
-        if (nhc > 3) {
-            // I above 3072: the persistent kernel's registers would spill.
-            const int nch = (a.I / 32 + 63) / 64;
-            const dim3 grid((unsigned)((int64_t)a.T * (a.H / 4))), block(kGemvWaves2 * 64);
-            if (nch == 1) hipLaunchKernelGGL((stage2_gemv_tok_kernel<1>), grid, block, 0, s, a);
-            else hipLaunchKernelGGL((stage2_gemv_tok_kernel<2>), grid, block, 0, s, a);
-        } else {
-            // About one workgroup per CU: G runs of R rows per token.
-            int G = 256 / a.T;
-            int R = (a.H + G - 1) / G;
-            R = R < 4 ? 4 : R > kRowsMax ? kRowsMax : R;
-            G = (a.H + R - 1) / R;
-            const int64_t nwg = (int64_t)a.T * G;
-            const dim3 grid((unsigned)((nwg + 7) / 8 * 8)), block(a.topk * 64);
-            if (nhc == 1) hipLaunchKernelGGL((stage2_gemv_rows_kernel<1>), grid, block, 0, s, a, G, R);
-            else if (nhc == 2) hipLaunchKernelGGL((stage2_gemv_rows_kernel<2>), grid, block, 0, s, a, G, R);
-            else hipLaunchKernelGGL((stage2_gemv_rows_kernel<3>), grid, block, 0, s, a, G, R);
-        }
+        const int rows = a.T < a.bm ? a.T : a.bm;
+        if (nhc == 1) launch_down_blk<1>(a, rows, s);
+        else if (nhc == 2) launch_down_blk<2>(a, rows, s);
+        else if (nhc == 3) launch_down_blk<3>(a, rows, s);
+        else launch_down_blk<4>(a, rows, s);
     }
     return hipGetLastError();
 }

@@ -48,8 +48,7 @@ hipError_t launch_stage2(const MoeGemmArgs& a, hipStream_t s);
 // One-wave-per-tile decode kernels (block size 16 or 32); stage 1 or 2.
 hipError_t launch_decode_stage(const MoeGemmArgs& a, int stage, hipStream_t s);
 // GEMV-shaped decode kernels (blocks of at most 8 token rows, MXFP4, K a
-// multiple of 512 up to 4096). Their stage 2 also performs the combine and
-// writes `out`; h is stored by pair index.
+// multiple of 512 up to 4096). h and y are stored by pair index.
 bool gemv_eligible(const MoeGemmArgs& a);
 hipError_t launch_gemv_stage(const MoeGemmArgs& a, int stage, hipStream_t s);
 
