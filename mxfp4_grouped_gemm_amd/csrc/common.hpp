@@ -137,6 +137,10 @@ __device__ __forceinline__ u32x2 bld8s(rsrc_t r, uint32_t voff, uint32_t soff) {
     return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
 }
 
+__device__ __forceinline__ u32x4 bld16snt(rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kNt));
+}
+
 // Orders one wave's LDS writes before its later LDS reads (LDS executes a
 // wave's operations in order; this keeps the compiler from reordering them).
 __device__ __forceinline__ void wave_lds_sync() {
