@@ -167,6 +167,11 @@ __device__ __forceinline__ void pf_tile(const MoeGemmArgs& a, SH& sh, int e, int
     const int K = STAGE == 1 ? a.H : a.I;
     const int nchunks = K / kPfChunk;
     constexpr int SB = FMT == kFmtMxfp4 ? 1 : 2;  // bytes per group scale
+    // int4 in single-wave tiles: every MFMA k-step stays inside one 32-group
+    // (k-steps 0, 1 of a chunk take its first group, 2, 3 the second); the
+    // codes enter as code + 136 and the group's scale and the 136 * sum(x)
+    // correction are applied to the group's fp32 result (see the k-loop).
+    constexpr bool GS = FMT == kFmtInt4g32 && DIRECT;
 
     // --- activations: thread t moves row 32i + t/8, logical piece t%8 of
     // every 32-row block i; in LDS the piece sits at t%8 ^ ((row/2) % 8).
@@ -184,10 +189,10 @@ __device__ __forceinline__ void pf_tile(const MoeGemmArgs& a, SH& sh, int e, int
         const int p = sh.rows[nl];
         if (STAGE == 1) {
             ra = make_rsrc(a.x, (uint32_t)((int64_t)a.T * a.H * 2));
-            aoff[0] = (p >= 0 && p < P) ? (uint32_t)(p / a.topk) * (uint32_t)(2 * a.H) + 64u * half : kOob;
+            aoff[0] = (p >= 0 && p < P) ? (uint32_t)(p / a.topk) * (uint32_t)(2 * a.H) + (GS ? 32u : 64u) * half : kOob;
         } else {
             ra = make_rsrc(a.h, (uint32_t)(a.cap * a.I * 2));
-            aoff[0] = (p >= 0 && p < P) ? (uint32_t)(row0 + nl) * (uint32_t)(2 * a.I) + 64u * half : kOob;
+            aoff[0] = (p >= 0 && p < P) ? (uint32_t)(row0 + nl) * (uint32_t)(2 * a.I) + (GS ? 32u : 64u) * half : kOob;
         }
     } else if constexpr (STAGE == 1) {
         ra = make_rsrc(a.x, (uint32_t)((int64_t)a.T * a.H * 2));
@@ -259,11 +264,19 @@ __device__ __forceinline__ void pf_tile(const MoeGemmArgs& a, SH& sh, int e, int
     };
     // MFMA B operand of chunk j of the stage, block nb: row 32nb + nl,
     // logical piece 2j + half (16 bytes = one MX block of 32 codes).
+    // GS: dwords 2*half, 2*half + 1 of both groups of chunk j (k-step s takes
+    // dword s & 1 of group s >> 1).
     auto read_bchunk = [&](u32x4 (&dst)[2], int j) {
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) {
             const int r = 32 * nb + nl;
-            dst[nb] = *(const u32x4*)(wl + r * 128 + (((2 * j + half) ^ ((r >> 1) & 7)) << 4));
+            if constexpr (GS) {
+                const u32x2 g0 = *(const u32x2*)(wl + r * 128 + (((2 * j) ^ ((r >> 1) & 7)) << 4) + 8 * half);
+                const u32x2 g1 = *(const u32x2*)(wl + r * 128 + (((2 * j + 1) ^ ((r >> 1) & 7)) << 4) + 8 * half);
+                dst[nb] = u32x4{g0[0], g0[1], g1[0], g1[1]};
+            } else {
+                dst[nb] = *(const u32x4*)(wl + r * 128 + (((2 * j + half) ^ ((r >> 1) & 7)) << 4));
+            }
         }
     };
     auto read_scales = [&](svec (&dst)[2]) {
@@ -288,8 +301,13 @@ __device__ __forceinline__ void pf_tile(const MoeGemmArgs& a, SH& sh, int e, int
     auto decode = [&](uint32_t d, float sc) -> Bop {
         Bop r;
         if constexpr (FMT == kFmtMxfp4) r.hi = mxfp4x8_to_bf16(d, sc);
+        else if constexpr (GS) r.hi = int4x8_to_bf16_biased(d);
         else int4x8_to_bf16_hilo(d, sc, r.hi, r.lo);
         return r;
+    };
+    // GS: the bf16 group scale of weight block nb for k-step s of chunk u.
+    auto gscale = [&](const svec& w8, int u, int s) -> float {
+        return __uint_as_float(((w8[u] >> (16 * (s >> 1))) & 0xffffu) << 16);
     };
 
     // Activation ring: chunk k lives in slot k % DA from its load (DA chunks
@@ -317,7 +335,8 @@ __device__ __forceinline__ void pf_tile(const MoeGemmArgs& a, SH& sh, int e, int
     auto issue_ad = [&](int slot, int c) {
         const uint32_t so = (uint32_t)(kPfRowBytes * (c < nchunks ? c : nchunks - 1));
 #pragma unroll
-        for (int s4 = 0; s4 < 4; ++s4) ad[slot][s4] = bld16s(ra, aoff[0] + 16u * s4, so);
+        for (int s4 = 0; s4 < 4; ++s4)
+            ad[slot][s4] = bld16s(ra, aoff[0] + (GS ? 64u * (s4 >> 1) + 16u * (s4 & 1) : 16u * s4), so);
     };
     auto store_a = [&](int slot, int buf) {
 #pragma unroll
@@ -340,6 +359,8 @@ __device__ __forceinline__ void pf_tile(const MoeGemmArgs& a, SH& sh, int e, int
         for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
+    // GS: one group's products (codes + 136) and its activation row sums.
+    f32x16 gacc[2], gsum;
 
     // Activations: three LDS buffers; at step c, chunk c is read from buffer
     // c%3, chunk c+1 already sits in buffer (c+1)%3 (so the first operands of
@@ -439,6 +460,30 @@ __device__ __forceinline__ void pf_tile(const MoeGemmArgs& a, SH& sh, int e, int
                     n0 = decode(bnext[0][0], scale_of(sn[0], (u + 1) & 3));
                     n1 = decode(bnext[1][0], scale_of(sn[1], (u + 1) & 3));
                 }
+                if constexpr (GS) {
+                    // Group s >> 1 of the chunk: two k-steps into gacc / gsum,
+                    // then acc += scale * (gacc - 136 * gsum), exact per term
+                    // up to fp32 rounding of the group sums.
+                    const bf16x8 ai = perm_x_int4(__builtin_bit_cast(bf16x8, ad[u % DD][s]));
+                    const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
+                    const f32x16 zero = {};
+                    gacc[0] = mfma32(ai, b0.hi, (s & 1) ? gacc[0] : zero);
+                    gacc[1] = mfma32(ai, b1.hi, (s & 1) ? gacc[1] : zero);
+                    gsum = mfma32(ai, ones, (s & 1) ? gsum : zero);
+                    if (s & 1) {
+                        const float g0 = gscale(scur[0], u, s), g1 = gscale(scur[1], u, s);
+#pragma unroll
+                        for (int q = 0; q < 16; ++q) {
+                            acc[0][0][q] = fmaf(fmaf(-136.0f, gsum[q], gacc[0][q]), g0, acc[0][0][q]);
+                            acc[0][1][q] = fmaf(fmaf(-136.0f, gsum[q], gacc[1][q]), g1, acc[0][1][q]);
+                        }
+                        // Pin the update here: left to the compiler it was
+                        // sunk past later groups, whose products then needed
+                        // fresh accumulator registers (224 AGPRs, one wave per
+                        // SIMD).
+                        asm volatile("" : "+v"(acc[0][0]), "+v"(acc[0][1]));
+                    }
+                } else {
 #pragma unroll
                 for (int i = 0; i < NB; ++i) {
                     const bf16x8 ai = DIRECT ? __builtin_bit_cast(bf16x8, ad[u % DD][s])
@@ -449,6 +494,7 @@ __device__ __forceinline__ void pf_tile(const MoeGemmArgs& a, SH& sh, int e, int
                         acc[i][0] = mfma32(ai, b0.lo, acc[i][0]);
                         acc[i][1] = mfma32(ai, b1.lo, acc[i][1]);
                     }
+                }
                 }
                 // Interleave: each MFMA pair is followed by an operand read
                 // and a couple of converts for the next step (and at s = 0 by

@@ -249,13 +249,15 @@ def test_forward_ragged_shapes(moe, T, H, I, E, topk, bm):
     (1, 8, 3, 512, 1024), (2, 6, 4, 512, 1024), (3, 5, 5, 512, 1024), (4, 16, 2, 512, 1024),
     (1, 8, 3, 512, 2048),    # two 64-lane chunks of half-blocks in the down kernel
     (2, 5, 5, 1024, 1536),   # the second chunk half used
-    (3, 6, 4, 512, 3072),    # three chunks; runs of 7 down rows end in a partial 4-row step
-    (4, 16, 16, 512, 3072),  # 16 slots: one wave per slot, 1024 threads
-    (1, 6, 4, 512, 4096),    # I above 3072: the 8-wave down kernel
+    (3, 6, 4, 512, 3072),    # three chunks of half-blocks (the production I)
+    (4, 16, 16, 512, 3072),  # 16 slots per token in the combine
+    (1, 6, 4, 512, 4096),    # four chunks of half-blocks
     (7, 16, 4, 512, 1024),   # 5..8 tokens: rows reloaded in sequence up to 8 per block
     (8, 8, 8, 512, 2048),    # topk == E: every block holds all 8 tokens
     (6, 12, 6, 1024, 1536),
-    (8, 4, 1, 512, 1024),    # topk 1: one wave per workgroup sums up to 128 down rows
+    (8, 4, 1, 512, 1024),    # topk 1: one pair per token
+    (2, 40, 20, 512, 1024),  # topk above 16
+    (1, 64, 32, 512, 1536),  # 32 slots of one token in the combine
 ])
 def test_forward_gemv_path_small(moe, T, E, topk, H, I):
     """Decode blocks of at most 8 token rows with K a multiple of 512 take the
@@ -531,7 +533,7 @@ def test_zero_tokens_is_noop(moe):
 
 @pytest.mark.parametrize("T,H,I,E,k,fused", [
     (7, 512, 256, 16, 4, False),   # separate route and sort calls, wave-per-tile kernels
-    (1, 512, 1024, 16, 4, True),   # fused small routing, GEMV gate_up, persistent down
+    (1, 512, 1024, 16, 4, True),   # fused small routing, GEMV gate_up and down, combine
     (8, 512, 256, 8, 4, True),     # single-wave MFMA tiles
     (40, 512, 256, 8, 4, True),    # workgroup routing, 4-wave tiles with super-blocks
 ])
