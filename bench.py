@@ -188,7 +188,7 @@ def stage1_kernel_name(T, bm, fmt, H, I, topk, E):
     gemv_eligible / forward_stages in the C sources, restated for the label)."""
     rows = min(T, bm)
     if (bm <= 32 and fmt == 0 and rows <= 8 and H <= 4096 and I <= 4096
-            and H % 512 == 0 and I % 512 == 0):
+            and H % 256 == 0 and I % 128 == 0):
         return "stage1_gemv_kernel"
     P = T * topk
     if bm == 32 and H % 256 == 0 and I % 256 == 0 and P >= 32:

@@ -1,5 +1,6 @@
 // GEMV-shaped decode kernels for expert blocks of at most 8 token rows
-// (MXFP4 weights, K a multiple of 512 up to 4096).
+// (MXFP4 weights; H a multiple of 256 and I a multiple of 128, both up to
+// 4096, so that each wave's scale bytes arrive as whole 16-byte pieces).
 //
 // With one or a few activation rows per expert block, 15/16 of every MFMA
 // would idle and the MFMA operand layout (16 rows x 64 bytes per load) costs a
@@ -331,7 +332,7 @@ __global__ __launch_bounds__(kDownWaves * 64) void stage2_gemv_blk_kernel(MoeGem
 bool gemv_eligible(const MoeGemmArgs& a) {
     const int max_rows = a.T < a.bm ? a.T : a.bm;
     return a.fmt == kFmtMxfp4 && max_rows <= 8 &&
-           a.H <= 4096 && a.I <= 4096 && a.H % 512 == 0 && a.I % 512 == 0 &&
+           a.H <= 4096 && a.I <= 4096 && a.H % 256 == 0 && a.I % 128 == 0 &&
            (int64_t)a.T * a.topk * a.I * 2 < 0x7fff0000LL;
 }
 

@@ -47,8 +47,9 @@ hipError_t launch_stage1(const MoeGemmArgs& a, hipStream_t s);
 hipError_t launch_stage2(const MoeGemmArgs& a, hipStream_t s);
 // One-wave-per-tile decode kernels (block size 16 or 32); stage 1 or 2.
 hipError_t launch_decode_stage(const MoeGemmArgs& a, int stage, hipStream_t s);
-// GEMV-shaped decode kernels (blocks of at most 8 token rows, MXFP4, K a
-// multiple of 512 up to 4096). h and y are stored by pair index.
+// GEMV-shaped decode kernels (blocks of at most 8 token rows, MXFP4, H a
+// multiple of 256 and I of 128, both up to 4096). h and y are stored by pair
+// index.
 bool gemv_eligible(const MoeGemmArgs& a);
 hipError_t launch_gemv_stage(const MoeGemmArgs& a, int stage, hipStream_t s);
 

@@ -258,10 +258,13 @@ def test_forward_ragged_shapes(moe, T, H, I, E, topk, bm):
     (8, 4, 1, 512, 1024),    # topk 1: one pair per token
     (2, 40, 20, 512, 1024),  # topk above 16
     (1, 64, 32, 512, 1536),  # 32 slots of one token in the combine
+    (1, 16, 4, 768, 384),    # I = 384 (the 8-way tensor-parallel shard): 24 half-blocks
+    (4, 12, 3, 256, 128),    # smallest H and I on this path: one lane's scales per pair
+    (8, 16, 6, 1280, 640),   # H, I not multiples of 512
 ])
 def test_forward_gemv_path_small(moe, T, E, topk, H, I):
-    """Decode blocks of at most 8 token rows with K a multiple of 512 take the
-    GEMV-shaped kernels; H=512 keeps the oracle fast."""
+    """Decode blocks of at most 8 token rows (H a multiple of 256, I of 128)
+    take the GEMV-shaped kernels; small H keeps the oracle fast."""
     wl = synth.small(T=T, H=H, I=I, E=E, topk=topk, seed=40 + T + I)
     out = run_layer(moe, wl, topk)
     ids, w = oracle.route_topk(wl.logits, topk)
