@@ -5,9 +5,9 @@
 //
 // One thread per 4 output columns. For topk <= 16 a workgroup owns 1024
 // columns of one token and all slot rows are fetched at once with branch-
-// free buffer loads (a slot whose expert id is outside [0, E) was never
-// placed by the sort; its load gets an out-of-range offset and contributes
-// zero): the ids come in with scalar loads, then one vector round trip.
+// free buffer loads, together with the slot ids and weights (a slot whose
+// expert id is outside [0, E) was never placed by the sort and contributes
+// zero): one vector round trip.
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -19,35 +19,41 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
                                                       const float* __restrict__ weights, int T,
                                                       int H, int E, int topk,
                                                       uint16_t* __restrict__ out) {
-    // Workgroup = (token t, 1024 columns): the token's slot ids and weights
-    // are the same for every lane, so they come in with scalar loads and the
-    // slot masks are uniform.
+    // Workgroup = (token t, 1024 columns).
     const int cblocks = (H + 1023) / 1024;
     const int t = (int)(blockIdx.x / cblocks);
     const int n = ((int)(blockIdx.x % cblocks) * 256 + (int)threadIdx.x) * 4;
     const int64_t P = (int64_t)T * topk;
     const rsrc_t ry = make_rsrc(y, (uint32_t)(P * H * 4));
+    // The token's slot ids and weights arrive as one vector load each (lane
+    // j holds slot j) together with the y rows, whose offsets depend only on
+    // the slot: one memory round trip. Slots past topk get an out-of-range
+    // row; a row whose id is outside [0, E) was never written and is
+    // replaced by zeros after the load.
+    const int lane = (int)threadIdx.x & 63;
+    const int64_t p0 = (int64_t)t * topk;
+    const int jl = lane < topk ? lane : topk - 1;
+    const int id_l = ids[p0 + jl];
+    const float w_l = weights[p0 + jl];
     f32x4 v[KMAX];
-    float wj[KMAX];
-    // Branch-free, so that every load is issued before the first wait: slots
-    // past topk re-read the last slot's id and weight and get weight 0 and an
-    // out-of-range row (adding 0 * 0 leaves the sum unchanged).
 #pragma unroll
     for (int j = 0; j < KMAX; ++j) {
-        const int64_t p = (int64_t)t * topk + (j < topk ? j : topk - 1);
-        const int e = ids[p];
-        const float w = weights[p];
-        const bool ok = j < topk && (unsigned)e < (unsigned)E;
-        wj[j] = ok ? w : 0.0f;
-        const uint32_t off = (ok && n < H) ? (uint32_t)((p * H + n) * 4) : kOob;
+        const uint32_t off = (j < topk && n < H) ? (uint32_t)(((p0 + j) * H + n) * 4) : kOob;
         v[j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ry, off, 0, 0));
     }
     if (n >= H) return;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < KMAX; ++j)
+    for (int j = 0; j < KMAX; ++j) {
+        const int e = __builtin_amdgcn_readlane(id_l, j);
+        const float wj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w_l), j));
+        const bool ok = j < topk && (unsigned)e < (unsigned)E;
+        const f32x4 vj = ok ? v[j] : zero;
+        const float w = ok ? wj : 0.0f;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] = fmaf(wj[j], v[j][i], acc[i]);
+        for (int i = 0; i < 4; ++i) acc[i] = fmaf(w, vj[i], acc[i]);
+    }
     u32x2 o;
     o[0] = pack_bf16x2(acc[0], acc[1]);
     o[1] = pack_bf16x2(acc[2], acc[3]);
