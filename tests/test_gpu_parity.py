@@ -261,6 +261,8 @@ def test_forward_ragged_shapes(moe, T, H, I, E, topk, bm):
     (1, 16, 4, 768, 384),    # I = 384 (the 8-way tensor-parallel shard): 24 half-blocks
     (4, 12, 3, 256, 128),    # smallest H and I on this path: one lane's scales per pair
     (8, 16, 6, 1280, 640),   # H, I not multiples of 512
+    (2, 4, 2, 4096, 512),    # largest H on this path: two full 64-lane chunks of MX blocks
+    (1, 2, 1, 4096, 4096),   # largest H and I together
 ])
 def test_forward_gemv_path_small(moe, T, E, topk, H, I):
     """Decode blocks of at most 8 token rows (H a multiple of 256, I of 128)
