@@ -46,7 +46,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode_t1",
                     help="decode_t1 (default), decode_t{4,7,16,32}, skewed_t{4,7,16,32}, "
-                         "prefill_t1024, int4_t16")
+                         "prefill_t1024, int4_t16, tp8_t1 (8-way tensor-parallel shard: E=896, I=384)")
     ap.add_argument("--sets", type=int, default=8, help="independent weight sets / routings")
     ap.add_argument("--eager", action="store_true", help="time eager launches, not graph replay")
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -26,6 +26,10 @@ import torch
 # The production expert-parallel shape validated on the MXFP4-to-int4 pull
 # request page (Validation: model_dim, intermediate_dim, local experts, topk).
 PROD = dict(H=3584, I=3072, E=112, topk=15)
+# One rank's share of the same model under 8-way tensor parallelism instead:
+# every expert (8 x 112), each with I / 8 = 384 (the same page's memory
+# comparison runs TP8 without expert parallelism).
+TP8 = dict(H=3584, I=384, E=896, topk=15)
 
 
 @dataclass
@@ -63,6 +67,7 @@ def specs():
         "decode_t1": Spec("decode_t1", T=1, seed=1, **PROD),
         "prefill_t1024": Spec("prefill_t1024", T=1024, seed=3, **PROD),
         "int4_t16": Spec("int4_t16", T=16, seed=4, **PROD),
+        "tp8_t1": Spec("tp8_t1", T=1, seed=5, **TP8),
     }
     for T in (4, 7, 16, 32):
         out[f"decode_t{T}"] = Spec(f"decode_t{T}", T=T, seed=100 + T, **PROD)

@@ -362,7 +362,7 @@ def _sample_tokens(T, n=4, seed=0):
 
 
 FULL = ["decode_t1", "decode_t4", "decode_t7", "decode_t16", "decode_t32", "skewed_t4", "skewed_t32",
-        "prefill_t1024"]
+        "prefill_t1024", "tp8_t1"]
 
 
 @pytest.fixture(scope="module")
