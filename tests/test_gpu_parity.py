@@ -199,6 +199,33 @@ def test_route_align_small_matches_oracle(moe, T, E, topk, bm):
     assert np.array_equal(off.cpu().numpy(), roff)
 
 
+@pytest.mark.parametrize("E,topk,renorm,ties", [(896, 15, True, False), (1024, 16, True, False),
+                                                (513, 15, True, False), (1000, 1, True, False),
+                                                (896, 15, False, False), (896, 16, True, True),
+                                                (640, 7, False, True), (512, 15, True, False)])
+def test_route_align_one_token_many_experts(moe, E, topk, renorm, ties):
+    """One token over more than 512 experts is routed by the whole workgroup
+    (candidates per wave, ranked by one wave): ids and weights equal the
+    single-wave routing of moe_route_topk bit for bit, and the oracle's."""
+    rng = np.random.default_rng(E + topk)
+    if ties:
+        logits = rng.integers(-3, 4, size=(1, E)).astype(np.float32)
+    else:
+        logits = rng.standard_normal((1, E)).astype(np.float32) * 2
+    ids, w, s, be, off, npp = moe.moe_route_align(dev(logits), topk, E, 16, renormalize=renorm)
+    ids1, w1 = moe.moe_route_topk(dev(logits), topk, renormalize=renorm)
+    torch.cuda.synchronize()
+    rids, rw = oracle.route_topk(logits, topk, renormalize=renorm)
+    assert np.array_equal(ids.cpu().numpy(), rids)
+    assert np.array_equal(ids1.cpu().numpy(), rids)
+    assert np.array_equal(w.cpu().numpy().view(np.uint32), w1.cpu().numpy().view(np.uint32))
+    np.testing.assert_allclose(w.cpu().numpy(), rw, rtol=1e-6, atol=1e-7)
+    rs, rbe, roff, rnpp = oracle.align_sort(rids, E, 16)
+    assert int(npp.item()) == rnpp
+    assert np.array_equal(s.cpu().numpy(), rs)
+    assert np.array_equal(off.cpu().numpy(), roff)
+
+
 def test_align_sort_drops_out_of_range_ids(moe):
     ids = np.array([[0, 5], [9, 1], [-1, 3]], dtype=np.int32)
     s, be, off, npp = moe.moe_align_sort(dev(ids), 6, 16)
