@@ -144,9 +144,12 @@ __global__ __launch_bounds__(kSortThreads) void route_align_kernel(
     __shared__ SortShared sh;
     __shared__ int32_t ids_lds[kFusedMaxPairs];
     const int wv = threadIdx.x >> 6;
+    // The routing scratch aliases the sort's mask table, which is written only
+    // after the barrier below.
     for (int t = wv; t < T; t += kSortWaves)
         route_token<VPL>(logits + (int64_t)t * E, E, topk, renorm, ids + (int64_t)t * topk,
-                         weights + (int64_t)t * topk, ids_lds + t * topk);
+                         weights + (int64_t)t * topk, ids_lds + t * topk,
+                         reinterpret_cast<uint64_t*>(sh.masks) + wv * 128);
     __syncthreads();
     align_sort_body(sh, ids_lds, T * topk, E, bm, cap, sorted_ids, block_expert, expert_offsets,
                     num_post_pad);
@@ -185,6 +188,7 @@ __global__ __launch_bounds__(NW * 64) void route_align_small_kernel(
     __shared__ int32_t start[kMaxExperts];
     __shared__ int32_t srt[kSmallCapMax];
     __shared__ int32_t blk[kSmallCapMax / 16];
+    __shared__ uint64_t rk[NW][64 * VPL <= 128 ? 64 * VPL : 1];  // routing scratch per wave
     const int tid = threadIdx.x;
     const int wv = tid >> 6;
     const int lane = tid & 63;
@@ -199,7 +203,7 @@ __global__ __launch_bounds__(NW * 64) void route_align_small_kernel(
     } else {
         for (int t = wv; t < T; t += NW)
             route_token<VPL>(logits + (int64_t)t * E, E, topk, renorm, ids + (int64_t)t * topk,
-                             weights + (int64_t)t * topk, ids_lds + t * topk);
+                             weights + (int64_t)t * topk, ids_lds + t * topk, rk[wv]);
     }
     __syncthreads();
     for (int p = tid; p < P; p += NT) {

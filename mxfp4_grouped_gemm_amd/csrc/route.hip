@@ -9,10 +9,11 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
                                                          int E, int topk, int renorm,
                                                          int32_t* __restrict__ ids,
                                                          float* __restrict__ weights) {
+    __shared__ uint64_t rk[4][64 * VPL <= 128 ? 64 * VPL : 1];
     const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
     route_token<VPL>(logits + (int64_t)t * E, E, topk, renorm, ids + (int64_t)t * topk,
-                     weights + (int64_t)t * topk, nullptr);
+                     weights + (int64_t)t * topk, nullptr, rk[threadIdx.x >> 6]);
 }
 
 hipError_t launch_route_topk(const float* logits, int T, int E, int topk, int renorm, int32_t* ids,

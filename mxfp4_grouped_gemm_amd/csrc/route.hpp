@@ -29,12 +29,34 @@ __device__ __forceinline__ float route_key_value(uint32_t k) {
 
 __device__ __forceinline__ int wave_popc(bool pred) { return __popcll(__ballot(pred)); }
 
+template <int CTRL>
+__device__ __forceinline__ uint32_t ror_max_u32(uint32_t v) {
+    const uint32_t o = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+    return v > o ? v : o;
+}
+
+// Maximum over the wave (all 64 lanes active).
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = ror_max_u32<0x128>(v);  // row_ror:8
+    v = ror_max_u32<0x124>(v);  // row_ror:4
+    v = ror_max_u32<0x122>(v);  // row_ror:2
+    v = ror_max_u32<0x121>(v);  // row_ror:1 -- every lane holds its row's maximum
+    uint32_t m = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+    const uint32_t m1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+    const uint32_t m2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+    const uint32_t m3 = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+    m = m1 > m ? m1 : m;
+    m = m2 > m ? m2 : m;
+    return m3 > m ? m3 : m;
+}
+
 // Routes one token with one wave. Lane-local slots i hold expert lane + 64 i
 // (VPL * 64 >= E). Writes ids[rank] and weights[rank] for rank < topk.
+// rk: this wave's LDS scratch of 64 * VPL entries (used when VPL <= 2).
 template <int VPL>
 __device__ __forceinline__ void route_token(const float* __restrict__ row, int E, int topk, int renorm,
                                             int32_t* __restrict__ ids, float* __restrict__ weights,
-                                            int32_t* __restrict__ ids_lds) {
+                                            int32_t* __restrict__ ids_lds, uint64_t* __restrict__ rk) {
     const int lane = threadIdx.x & 63;
     float val[VPL];
     uint32_t key[VPL];
@@ -46,6 +68,37 @@ __device__ __forceinline__ void route_token(const float* __restrict__ row, int E
         val[i] = ok[i] ? row[e] : 0.0f;
         key[i] = route_key(val[i]);
     }
+    bool sel[VPL];
+    int rank[VPL];
+    uint32_t kmax = 0u;
+    if constexpr (VPL <= 2) {
+    // Up to 128 experts: every lane counts, for each of its experts, the
+    // experts ranked before it -- larger key, or equal key and lower index:
+    // one 64-bit compare of (key, ~index) against each entry of the token's
+    // keys in wave-private LDS (broadcast reads). No scalar chains.
+    uint64_t* kk = rk;
+    uint64_t k64[VPL];
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+        const uint32_t e = (uint32_t)(lane + 64 * i);
+        k64[i] = ok[i] ? ((uint64_t)key[i] << 32) | (uint64_t)~e : 0ull;
+        kk[e] = k64[i];
+        rank[i] = 0;
+    }
+    wave_lds_sync();
+    for (int j = 0; j < E; j += 2) {
+        const uint64_t kj0 = kk[j], kj1 = kk[j + 1];  // entries up to 64 * VPL hold 0 past E
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) rank[i] += (kj0 > k64[i] ? 1 : 0) + (kj1 > k64[i] ? 1 : 0);
+    }
+    wave_lds_sync();  // the next token's keys overwrite this wave's entries
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+        sel[i] = ok[i] && rank[i] < topk;
+        if (sel[i] && rank[i] == 0) kmax = key[i];
+    }
+    kmax = wave_max_u32(kmax);
+    } else {
     // k-th largest key: the largest T with count(key >= T) >= topk, two key
     // bits per round (three independent counts). Slots past E get key 0,
     // which no candidate (always >= 1) counts.
@@ -70,7 +123,6 @@ __device__ __forceinline__ void route_token(const float* __restrict__ row, int E
     for (int i = 0; i < VPL; ++i) above += wave_popc(ok[i] && key[i] > thr);
     // Keep everything above thr, then ties at thr in index order (slot-major).
     int need = topk - above;
-    bool sel[VPL];
     const uint64_t below_me = (1ull << lane) - 1ull;
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
@@ -83,10 +135,8 @@ __device__ __forceinline__ void route_token(const float* __restrict__ row, int E
     }
     // Rank the kept experts: by key descending, then index ascending. The
     // largest kept key gives the softmax shift.
-    int rank[VPL];
 #pragma unroll
     for (int i = 0; i < VPL; ++i) rank[i] = 0;
-    uint32_t kmax = 0u;
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
         uint64_t m = __ballot(sel[i]);
@@ -102,6 +152,7 @@ __device__ __forceinline__ void route_token(const float* __restrict__ row, int E
                 rank[j] += (kv > key[j] || (kv == key[j] && ev < e)) ? 1 : 0;
             }
         }
+    }
     }
     const float lmax = route_key_value(kmax);
     float ex[VPL];
