@@ -5,11 +5,15 @@
 // topk (equal logits: lower index first), weight them by their softmax
 // probabilities, renormalised over the kept experts on request.
 //
-// Selection is a radix select over order-preserving 32-bit keys: 16 rounds of
-// (compare, ballot, popcount) over two key bits find the k-th largest key; keys above it are
-// kept and the ties at it are taken lowest index first. The kept experts are
-// then ranked against each other in a scalar loop of at most topk steps.
-// Everything stays in registers and SGPRs; no cross-lane shuffles through LDS.
+// Up to 128 experts, every lane ranks its own experts directly: it counts
+// the experts ordered before each of them (larger key, or equal key and lower
+// index) against the token's keys in the wave's LDS scratch, and keeps those
+// ranked below topk. For more experts, selection is a radix select over
+// order-preserving 32-bit keys: 16 rounds of (compare, ballot, popcount) over
+// two key bits find the k-th largest key; keys above it are kept and the
+// ties at it are taken lowest index first; the kept experts are then ranked
+// against each other in a scalar loop of at most topk steps. Above 512
+// experts a single token is routed by a whole workgroup (route_token_wg).
 #pragma once
 
 #include "common.hpp"
