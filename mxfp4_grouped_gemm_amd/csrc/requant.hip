@@ -105,8 +105,9 @@ __global__ __launch_bounds__(256) void requant_kernel(const uint8_t* __restrict_
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < ngroups;
          i += (int64_t)gridDim.x * 256) {
         const int64_t gi = g0 + i;
-        const u32x4 d = *(const u32x4*)(w + gi * 16);
-        const uint32_t sb = scale[gi];
+        // Every byte is read and written once: streaming (nt) accesses.
+        const u32x4 d = __builtin_nontemporal_load((const u32x4*)(w + gi * 16));
+        const uint32_t sb = __builtin_nontemporal_load(scale + gi);
         u32x4 packed = {0u, 0u, 0u, 0u};
         uint16_t sbits;
         if (sb >= 5u && sb <= 252u) {
@@ -152,8 +153,8 @@ __global__ __launch_bounds__(256) void requant_kernel(const uint8_t* __restrict_
                 }
             }
         }
-        *(u32x4*)(q + gi * 16) = packed;
-        qs[gi] = sbits;
+        __builtin_nontemporal_store(packed, (u32x4*)(q + gi * 16));
+        __builtin_nontemporal_store(sbits, qs + gi);
     }
 }
 
