@@ -14,7 +14,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe_a16w4.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["abi.cpp", "route.hip", "align_sort.hip", "gemm_stream.hip", "gemm_decode.hip", "gemm_gemv.hip", "gemm_prefill.hip", "combine.hip", "requant.hip"]
+SOURCES = ["abi.cpp", "route.hip", "align_sort.hip", "gemm_stream.hip", "gemm_decode.hip", "gemm_gemv.hip", "gemm_prefill.hip", "gemm_prefill_int4.hip", "combine.hip", "requant.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
@@ -23,10 +23,17 @@ FLAGS = [
 ]
 
 
+# Per-file extra flags. The int4 single-wave tiles read their MFMA results
+# back every 32-group; with the results in VGPRs instead of AGPRs no
+# v_accvgpr_read is needed (the option must not reach the 4-wave kernels,
+# which need AGPRs for 256 accumulator registers).
+FILE_FLAGS = {"gemm_prefill_int4.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
     lang = ["-x", "hip"] if src.endswith(".cpp") else []
-    cmd = [HIPCC, *FLAGS, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *FILE_FLAGS.get(src, []), *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -45,13 +45,20 @@ __device__ __forceinline__ bf16x8 mxfp4x8_to_bf16(uint32_t d, float scale) {
 // the low mantissa bits of 128.0 (bf16 0x4300, ulp 1). Output element
 // order: nibbles {0, 4, 1, 5, 2, 6, 3, 7} -- the activation operand must use
 // the same permutation (see perm_x_int4).
+//
+// One v_bitop3 per output dword (after a shift): with s = d >> 4i, bit p of
+// the result is 1 where 0x4300 has ones, NOT s[p] at the nibble's top bit
+// (code ^ 8), s[p] at its three low bits and 0 elsewhere. The two constant
+// operands mark these four kinds of positions (B: "1" or "not s", C: "1" or
+// "s"), and the truth table 0xAC selects: B C = 00 -> 0, 01 -> s, 10 -> !s,
+// 11 -> 1 (table index = 4 s + 2 B + C).
 __device__ __forceinline__ bf16x8 int4x8_to_bf16_biased(uint32_t d) {
-    const uint32_t u = d ^ 0x88888888u;
+    constexpr uint32_t kB = 0x43084308u, kC = 0x43074307u;
     u32x4 r;
-    r[0] = (u & 0x000F000Fu) | 0x43004300u;
-    r[1] = ((u >> 4) & 0x000F000Fu) | 0x43004300u;
-    r[2] = ((u >> 8) & 0x000F000Fu) | 0x43004300u;
-    r[3] = ((u >> 12) & 0x000F000Fu) | 0x43004300u;
+    r[0] = __builtin_amdgcn_bitop3_b32(d, kB, kC, 0xAC);
+    r[1] = __builtin_amdgcn_bitop3_b32(d >> 4, kB, kC, 0xAC);
+    r[2] = __builtin_amdgcn_bitop3_b32(d >> 8, kB, kC, 0xAC);
+    r[3] = __builtin_amdgcn_bitop3_b32(d >> 12, kB, kC, 0xAC);
     return __builtin_bit_cast(bf16x8, r);
 }
 
