@@ -1,6 +1,8 @@
-// Prefill-sized grouped GEMMs (MXFP4 weights, bf16 MFMA): the super-block
-// pass, the 4-wave kernels and the launcher. The tile design is described
-// in prefill_tile.hpp.
+// Prefill-sized grouped GEMMs (bf16 MFMA over MXFP4 or int4-g32 weights):
+// the super-block pass, the 4-wave kernels, the launcher and (through it) the
+// MXFP4 single-wave kernels. The tile design is described in
+// prefill_tile.hpp; the int4 single-wave kernels are built in
+// gemm_prefill_int4.hip.
 #include "prefill_tile.hpp"
 
 namespace moe {
