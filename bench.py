@@ -192,7 +192,7 @@ def stage1_kernel_name(T, bm, fmt, H, I, topk, E):
         return "stage1_gemv_kernel"
     P = T * topk
     if bm == 32 and H % 256 == 0 and I % 256 == 0 and P >= 32:
-        if T <= 16:
+        if T <= (13 if fmt == 0 else 32):
             return f"prefill_direct_kernel<1, {fmt}>"
         return f"prefill_kernel<1, {fmt}, 2>" if P <= 48 * min(P, E) else f"prefill_kernel<1, {fmt}, 8>"
     return "stage1_unit_kernel" if bm <= 32 else "stage1_stream_kernel"

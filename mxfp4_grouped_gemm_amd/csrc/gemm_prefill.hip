@@ -115,7 +115,9 @@ int64_t prefill_list_bytes(int64_t cap) { return (cap / kPfBlockRows + 1) * 16 +
 hipError_t launch_prefill(const MoeGemmArgs& a, int stage, void* list_ws, hipStream_t s) {
     int4* list = (int4*)list_ws;
     const int64_t nblocks = a.cap / kPfBlockRows;
-    if (a.T <= (stage == 1 ? kPfDirectMaxTokens1 : kPfDirectMaxTokens2)) {
+    const int direct_max = stage == 2 ? kPfDirectMaxTokens2
+                           : a.fmt == kFmtMxfp4 ? kPfDirectMaxTokens1 : kPfDirectMaxTokens1Int4;
+    if (a.T <= direct_max) {
         const int ntiles = stage == 1 ? a.I / 32 : a.H / 64;
         const dim3 grid((unsigned)(8 * ((nblocks + 7) / 8) * ntiles)), block(64);
         if (a.fmt == kFmtMxfp4) {

@@ -63,10 +63,13 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int kPfWRows = 64;
 constexpr int kPfStage = 4;  // chunks per weight stage
 // Single-wave tiles up to this many tokens (at most one 32-row block per
-// expert needs T <= 32). For gate_up, above 16 tokens the blocks fill up and
-// the 4-wave tiles, which share each activation chunk between four waves,
-// are faster; for down the single-wave tiles stay ahead up to 32.
-constexpr int kPfDirectMaxTokens1 = 16;
+// expert needs T <= 32). For MXFP4 gate_up, from 14 tokens on the blocks
+// fill up and the 4-wave tiles, which share each activation chunk between
+// four waves, are faster (1-2 % at 14-16 tokens); int4 gate_up and both
+// formats' down stay on the single-wave tiles up to 32 (the 4-wave int4
+// tiles split every weight into two MFMAs: 548 against 305 us at 24 tokens).
+constexpr int kPfDirectMaxTokens1 = 13;
+constexpr int kPfDirectMaxTokens1Int4 = 32;
 constexpr int kPfDirectMaxTokens2 = 32;
 template <int NBMAX>
 struct __attribute__((aligned(16))) PfShared {

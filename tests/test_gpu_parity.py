@@ -331,12 +331,17 @@ def test_forward_prefill_path(moe, T, H, I, E, topk, hot):
     (13, 768, 256, 4, 3, 0, 0),    # ragged T
     (16, 512, 256, 12, 3, 3, 0),   # skewed: hot experts hold every token
     (16, 512, 512, 8, 4, 0, 1),    # int4-g32 weights
-    (32, 512, 256, 12, 3, 3, 0),   # 17..32 tokens: 4-wave gate_up tiles, single-wave down tiles
+    (14, 512, 256, 16, 4, 0, 0),   # MXFP4 from 14 tokens: 4-wave gate_up tiles, single-wave down tiles
+    (32, 512, 256, 12, 3, 3, 0),   # the same at 32 tokens, skewed
+    (24, 768, 256, 12, 3, 3, 1),   # int4 up to 32 tokens: single-wave tiles for both stages, skewed
+    (32, 512, 512, 8, 4, 0, 1),    # int4 at 32 tokens: every block of 32 rows full
 ])
 def test_forward_direct_tiles(moe, T, H, I, E, topk, hot, fmt):
-    """Batches of up to 16 tokens sorted into 32-row blocks (at least 32
-    pairs) take single-wave MFMA tiles, one per (block, 64 weight rows);
-    every token is compared. (32-row blocks are the default above 8 tokens.)"""
+    """Batches of up to 32 tokens sorted into 32-row blocks (at least 32
+    pairs) take single-wave MFMA tiles, one per (block, 64 weight rows), for
+    down, int4 gate_up and MXFP4 gate_up up to 13 tokens (4-wave tiles from
+    14); every token is compared. (32-row blocks are the default above 8
+    tokens.)"""
     wl = synth.small(T=T, H=H, I=I, E=E, topk=topk, seed=11 * T + E + fmt, hot=hot)
     ids, w = oracle.route_topk(wl.logits, topk)
     if fmt == 0:
