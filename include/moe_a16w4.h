@@ -142,6 +142,11 @@ int64_t moe_a16w4_workspace_size(int T, int H, int I, int E, int topk, int block
  *   1 <= topk <= E, block_m in {16, 32, 64} (128 and 256 are valid sort
  *   sizes but give MOE_ERR_UNSUPPORTED here); all pointers 16-byte aligned
  *   (workspace 256-byte aligned).
+ * Size limits (MOE_ERR_UNSUPPORTED, nothing launched): x [T, H] and the
+ *   workspace's bf16 h [cap, I] (cap = moe_align_sort_capacity) must each
+ *   stay below 2^31 - 2^16 bytes, and with block_m == 64 cap / 64 <= 65535.
+ *   At H = 3584, I = 3072, E = 112, topk = 15, block_m = 32 that allows up
+ *   to about 23,000 tokens per call; larger batches are split by the caller.
  * MXFP4 e8m0 bytes must be in [0, 254]; weights whose value overflows bf16
  * give unspecified results. */
 moe_status moe_a16w4_forward(const uint16_t* x, const uint8_t* w13, const void* w13_scale,
@@ -188,7 +193,10 @@ moe_status moe_a16w4_forward_stages(const uint16_t* x, const uint8_t* w13, const
  *                   Only experts in [expert_lo, expert_hi) are written; the
  *                   library uses no scratch memory beyond these outputs.
  * Requirements: K % 32 == 0, N >= 1, 0 <= expert_lo <= expert_hi <= E;
- * pointers 16-byte aligned. Lossy by construction. */
+ * pointers 16-byte aligned. Lossy by construction.
+ * Domain: e8m0 bytes 0..252. Bytes 253..255 (decoded values that overflow
+ * bf16, or a NaN scale) give unspecified codes and scales, computed without
+ * faulting. */
 moe_status mxfp4_to_int4g32_requant(const uint8_t* w, const uint8_t* scale_e8m0, int E, int N,
                                     int K, int expert_lo, int expert_hi, uint8_t* w_int4,
                                     uint16_t* scale_bf16, void* stream);

@@ -17,6 +17,7 @@ in-kernel routing path of apply_monolithic on the vLLM mxfp4 API page) and
 requantize_mxfp4_experts (the chunked MXFP4 -> int4-g32 load-time
 conversion, eight experts per call).
 """
+import contextlib
 import ctypes
 import os
 import warnings
@@ -93,6 +94,13 @@ def _stream(stream=None):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _on(stream):
+    """Allocation context for the tensors a call creates: with an explicit
+    stream they are allocated on it, so the caching allocator does not hand
+    their memory to other work while the call's kernels still use it."""
+    return contextlib.nullcontext() if stream is None else torch.cuda.stream(stream)
+
+
 def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else None
 
@@ -115,10 +123,11 @@ def moe_route_topk(logits, topk, renormalize=True, topk_ids=None, topk_weights=N
     """Softmax top-k routing of fp32 logits [T, E] -> (ids int32, weights fp32) [T, topk]."""
     _dev(logits, "logits", torch.float32, 2)
     T, E = logits.shape
-    if topk_ids is None:
-        topk_ids = torch.empty((T, topk), dtype=torch.int32, device=logits.device)
-    if topk_weights is None:
-        topk_weights = torch.empty((T, topk), dtype=torch.float32, device=logits.device)
+    with _on(stream):
+        if topk_ids is None:
+            topk_ids = torch.empty((T, topk), dtype=torch.int32, device=logits.device)
+        if topk_weights is None:
+            topk_weights = torch.empty((T, topk), dtype=torch.float32, device=logits.device)
     _dev(topk_ids, "topk_ids", torch.int32)
     _dev(topk_weights, "topk_weights", torch.float32)
     _check(lib.moe_route_topk(_ptr(logits), T, E, int(topk), int(bool(renormalize)),
@@ -143,10 +152,11 @@ def moe_align_sort(topk_ids, E, block_m, out=None, stream=None):
         raise MoeError(MOE_ERR_INVALID_ARG, f"invalid align/sort sizes T={T} topk={topk} E={E} block_m={block_m}")
     dev = topk_ids.device
     if out is None:
-        out = (torch.empty(max(cap, 1), dtype=torch.int32, device=dev),
-               torch.empty(max(cap // block_m, 1), dtype=torch.int32, device=dev),
-               torch.empty(E + 1, dtype=torch.int32, device=dev),
-               torch.empty(1, dtype=torch.int32, device=dev))
+        with _on(stream):
+            out = (torch.empty(max(cap, 1), dtype=torch.int32, device=dev),
+                   torch.empty(max(cap // block_m, 1), dtype=torch.int32, device=dev),
+                   torch.empty(E + 1, dtype=torch.int32, device=dev),
+                   torch.empty(1, dtype=torch.int32, device=dev))
     sorted_ids, block_expert, offsets, npp = out
     if sorted_ids.numel() < cap or block_expert.numel() < cap // block_m or offsets.numel() < E + 1:
         raise ValueError("align/sort output buffers too small")
@@ -164,20 +174,22 @@ def moe_route_align(logits, topk, E, block_m, renormalize=True, ids=None, weight
     if El != E:
         raise ValueError(f"logits have {El} experts, expected {E}")
     dev = logits.device
-    if ids is None:
-        ids = torch.empty((T, topk), dtype=torch.int32, device=dev)
-    if weights is None:
-        weights = torch.empty((T, topk), dtype=torch.float32, device=dev)
+    with _on(stream):
+        if ids is None:
+            ids = torch.empty((T, topk), dtype=torch.int32, device=dev)
+        if weights is None:
+            weights = torch.empty((T, topk), dtype=torch.float32, device=dev)
     _dev(ids, "ids", torch.int32)
     _dev(weights, "weights", torch.float32)
     cap = moe_align_sort_capacity(T, topk, E, block_m)
     if cap < 0:
         raise MoeError(MOE_ERR_INVALID_ARG, f"invalid sizes T={T} topk={topk} E={E} block_m={block_m}")
     if out is None:
-        out = (torch.empty(max(cap, 1), dtype=torch.int32, device=dev),
-               torch.empty(max(cap // block_m, 1), dtype=torch.int32, device=dev),
-               torch.empty(E + 1, dtype=torch.int32, device=dev),
-               torch.empty(1, dtype=torch.int32, device=dev))
+        with _on(stream):
+            out = (torch.empty(max(cap, 1), dtype=torch.int32, device=dev),
+                   torch.empty(max(cap // block_m, 1), dtype=torch.int32, device=dev),
+                   torch.empty(E + 1, dtype=torch.int32, device=dev),
+                   torch.empty(1, dtype=torch.int32, device=dev))
     sorted_ids, block_expert, offsets, npp = out
     if sorted_ids.numel() < cap or block_expert.numel() < cap // block_m or offsets.numel() < E + 1:
         raise ValueError("align/sort output buffers too small")
@@ -220,14 +232,15 @@ def moe_a16w4_forward(x, w13, w13_scale, w2, w2_scale, topk_ids, topk_weights, s
     _dev(topk_ids, "topk_ids", torch.int32, 2)
     _dev(topk_weights, "topk_weights", torch.float32, 2)
     topk = topk_ids.shape[1]
-    if out is None:
-        out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
-    _dev(out, "out", torch.bfloat16)
     need = moe_a16w4_workspace_size(T, H, I, E, topk, block_m)
     if need < 0:
         raise MoeError(MOE_ERR_INVALID_ARG, "invalid forward sizes")
-    if workspace is None:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
+    with _on(stream):
+        if out is None:
+            out = torch.empty((T, H), dtype=torch.bfloat16, device=x.device)
+        if workspace is None:
+            workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
+    _dev(out, "out", torch.bfloat16)
     args = (_ptr(x), _ptr(w13), _ptr(w13_scale), _ptr(w2), _ptr(w2_scale), int(fmt), int(act),
             _ptr(topk_ids), _ptr(topk_weights), _ptr(sorted_ids), _ptr(block_expert),
             _ptr(num_post_pad), T, H, I, E, topk, int(block_m), _ptr(out), _ptr(workspace),
@@ -241,7 +254,11 @@ def moe_a16w4_forward(x, w13, w13_scale, w2, w2_scale, topk_ids, topk_weights, s
 
 def moe_a16w4_layer(x, router_logits, w13, w13_scale, w2, w2_scale, topk, fmt=MOE_W_MXFP4,
                     renormalize=True, block_m=None, stream=None):
-    """route -> align/sort -> forward on one stream (no host synchronisation)."""
+    """route -> align/sort -> forward on one stream (no host synchronisation).
+    With an explicit `stream` every tensor the call creates is allocated on
+    that stream (the routing and sort arrays, the workspace and the output),
+    so their memory stays reserved until the stream's work is done; the
+    caller orders any use of the output on another stream as usual."""
     E = w13.shape[0]
     T = x.shape[0]
     bm = moe_default_block_m(T, topk, E) if block_m is None else block_m
@@ -281,8 +298,9 @@ def requantize_mxfp4_experts(w, scale_e8m0, chunk=8, stream=None):
                       "this conversion is lossy.", stacklevel=2)
         _warned_lossy = True
     E, N, Kh = w.shape
-    codes = torch.empty_like(w)
-    scales = torch.empty((E, N, Kh * 2 // 32), dtype=torch.bfloat16, device=w.device)
+    with _on(stream):
+        codes = torch.empty_like(w)
+        scales = torch.empty((E, N, Kh * 2 // 32), dtype=torch.bfloat16, device=w.device)
     for lo in range(0, E, chunk):
         mxfp4_to_int4g32_requant(w, scale_e8m0, lo, min(lo + chunk, E), codes, scales, stream=stream)
     return codes, scales

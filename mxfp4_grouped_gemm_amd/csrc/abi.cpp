@@ -31,6 +31,12 @@ moe_status hip_status(hipError_t e, const char* what) {
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
+// Largest activation buffer (x or h) the GEMM kernels address with 32-bit
+// buffer offsets, keeping kOob (2^31) past the end of every record.
+constexpr int64_t kMaxRecordBytes = 0x7fff0000LL;
+// Blocks of the 64-row kernels run along grid.y.
+constexpr int64_t kMaxGridY = 65535;
+
 bool valid_bm(int bm) { return bm == 16 || bm == 32 || bm == 64 || bm == 128 || bm == 256; }
 
 // Block sizes the GEMM kernels are built for.
@@ -200,8 +206,18 @@ moe_status moe_a16w4_forward_stages(const uint16_t* x, const uint8_t* w13, const
         return fail(MOE_ERR_UNSUPPORTED, "%s: block_m=%d not implemented (16, 32, 64)", fn, block_m);
     const int64_t P = (int64_t)T * topk;
     const int64_t cap = capacity(T, topk, E, block_m);
-    if (P + cap >= (int64_t)0x7fffffff || (int64_t)T * H >= ((int64_t)1 << 40))
+    if (P + cap >= (int64_t)0x7fffffff)
         return fail(MOE_ERR_UNSUPPORTED, "%s: problem too large", fn);
+    // The activation kernels address x [T, H] and h [cap, I] through buffer
+    // records of at most 2^31 bytes (their masked lanes use offsets past
+    // 2^31), and the 64-row kernels index blocks by grid.y.
+    if ((int64_t)T * H * 2 > kMaxRecordBytes || cap * I * 2 > kMaxRecordBytes)
+        return fail(MOE_ERR_UNSUPPORTED,
+                    "%s: T=%d gives activations beyond 2^31 bytes (x %lld B, h %lld B); "
+                    "split the batch", fn, T, (long long)((int64_t)T * H * 2), (long long)(cap * I * 2));
+    if (block_m == 64 && cap / block_m > kMaxGridY)
+        return fail(MOE_ERR_UNSUPPORTED, "%s: %lld blocks of 64 rows exceed the grid", fn,
+                    (long long)(cap / block_m));
     if (T == 0) return MOE_OK;
     const void* ptrs[] = {x, w13, w13_scale, w2, w2_scale, topk_ids, topk_weights,
                           sorted_ids, block_expert, num_post_pad, out, workspace};

@@ -23,11 +23,14 @@ _lib = None
 
 
 def lib():
+    """The oracle library: oracle/libmoe_oracle.so (built on first use), or
+    the file MOE_ORACLE_LIB names (the sanitizer build of the same source)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(_build.LIB):
+        path = os.environ.get("MOE_ORACLE_LIB") or _build.LIB
+        if path == _build.LIB and not os.path.exists(path):
             _build.build()
-        L = ctypes.CDLL(_build.LIB)
+        L = ctypes.CDLL(path)
         p = ctypes.c_void_p
         i = ctypes.c_int
         L.oracle_e2m1_value.restype = ctypes.c_double

@@ -309,6 +309,12 @@ void oracle_requant_int4g32(const uint8_t* w, const uint8_t* scale_e8m0,
                     int q = 0;
                     if (sf != 0.0f) {
                         float r = rintf(v[i] / sf); /* ties to even */
+                        /* Outside the domain (e8m0 bytes 253-255, where the
+                         * decoded values overflow bf16) the quotient can be
+                         * inf / inf = NaN; such an element gets code 0 so the
+                         * oracle stays defined there (no float -> int
+                         * conversion of NaN). */
+                        if (isnan(r)) r = 0.0f;
                         if (r > 7.0f) r = 7.0f;
                         if (r < -8.0f) r = -8.0f;
                         q = (int)r;

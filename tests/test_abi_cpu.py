@@ -3,8 +3,13 @@
 * the library loads and exports every function include/moe_a16w4.h declares;
 * host logic: capacity, workspace size, default block size;
 * fail-closed validation: bad shapes, ranges, activations and formats return
-  an error status before any launch (null device pointers prove that no
-  kernel was enqueued -- the calls would fault otherwise).
+  an error status before any launch (the calls pass null or made-up device
+  pointers, which no kernel may ever see).
+
+This file runs only where no GPU is visible: if a validation check ever
+regressed, a call here would reach a launch, which without a device fails
+with a HIP error instead of touching memory. On a machine with a GPU the
+module is skipped, so those pointers can never reach a kernel.
 """
 import ctypes
 import os
@@ -15,6 +20,18 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "moe_a16w4.h")
+
+
+def _gpu_visible():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+pytestmark = pytest.mark.skipif(_gpu_visible(), reason="host-only checks pass invalid device "
+                                "pointers; never run where a GPU is visible")
 
 
 @pytest.fixture(scope="module")
@@ -112,3 +129,25 @@ def test_python_binding_rejects_host_tensors(moe):
     import torch
     with pytest.raises(ValueError):
         moe.moe_route_topk(torch.zeros(2, 8), 2)
+
+
+def test_forward_rejects_activations_beyond_32bit_records(moe):
+    """x [T, H] or h [cap, I] past what 32-bit buffer offsets address: the
+    call returns MOE_ERR_UNSUPPORTED before any launch. The pointers are
+    made-up aligned addresses; validation must stop before a kernel."""
+    fake = 1 << 20
+    ws = 1 << 40
+
+    def fwd(T, H=3584, I=3072, E=112, topk=15, bm=32):
+        return moe.lib.moe_a16w4_forward(fake, fake, fake, fake, fake, 0, 0, fake, fake, fake,
+                                         fake, fake, T, H, I, E, topk, bm, fake, fake, ws, None)
+    # about 23K tokens is the largest h at the production shape
+    assert fwd(50000) == moe.MOE_ERR_UNSUPPORTED
+    assert "2^31" in moe.moe_last_error()
+    assert fwd(24000) == moe.MOE_ERR_UNSUPPORTED
+    # x alone too large (small I keeps h in range)
+    assert fwd(300000, H=4096, I=32, E=8, topk=1) == moe.MOE_ERR_UNSUPPORTED
+    # 64-row blocks beyond grid.y
+    assert fwd(5000000, H=32, I=32, E=8, topk=1, bm=64) == moe.MOE_ERR_UNSUPPORTED
+    # capacities the sizes query accepts stay consistent with the guard
+    assert moe.moe_align_sort_capacity(23000, 15, 112, 32) * 3072 * 2 < 0x7fff0000
