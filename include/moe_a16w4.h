@@ -180,6 +180,34 @@ moe_status moe_a16w4_forward_stages(const uint16_t* x, const uint8_t* w13, const
                                     void* workspace, size_t workspace_bytes, unsigned stages,
                                     void* stream);
 
+/* moe_a16w4_forward without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc). The workspace is the library's
+ * own scratch array of MOE_NOALLOC_SCRATCH_BYTES on each GPU, reserved
+ * when the library's code is loaded on that GPU and held until the process
+ * ends; its device address is looked up on the first call on each device.
+ * The call allocates nothing (no hipMalloc/hipFree, no allocating library
+ * routine); the caller passes inputs and `out` as for moe_a16w4_forward.
+ *   - Same arguments, requirements and results as moe_a16w4_forward minus
+ *     workspace/workspace_bytes.
+ *   - A batch whose moe_a16w4_workspace_size exceeds the scratch returns
+ *     MOE_ERR_UNSUPPORTED before anything is enqueued (64 MiB holds the
+ *     workspace of up to about 128 tokens at H = 3584, I = 3072, E = 112,
+ *     topk = 15).
+ *   - Every call on one GPU shares that GPU's scratch and leaves its
+ *     contents behind; nothing in it needs to start at zero (each call
+ *     writes what it reads). Calls that overlap in time on one GPU (on
+ *     different streams, or from different threads) race on it and give
+ *     wrong results: order them on one stream. */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+moe_status moe_a16w4_forward_noalloc(const uint16_t* x, const uint8_t* w13, const void* w13_scale,
+                                     const uint8_t* w2, const void* w2_scale, moe_wfmt fmt,
+                                     moe_act act, const int32_t* topk_ids,
+                                     const float* topk_weights, const int32_t* sorted_ids,
+                                     const int32_t* block_expert, const int32_t* num_post_pad,
+                                     int T, int H, int I, int E, int topk, int block_m,
+                                     uint16_t* out, void* stream);
+
 /* MXFP4 -> int4 per-group-32 requantization of experts [expert_lo,
  * expert_hi) of a [E, N, K] weight (convert() in
  * Mxfp4MoEMethod._setup_kernel_k3_situ_gfx942; the pull request converts

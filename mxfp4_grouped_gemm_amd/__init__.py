@@ -10,7 +10,7 @@ library has not been built.
 Functions mirror the C ABI names:
   moe_route_topk, moe_align_sort_capacity, moe_default_block_m,
   moe_align_sort, moe_route_align, moe_a16w4_workspace_size, moe_a16w4_forward,
-  moe_a16w4_forward_stages,
+  moe_a16w4_forward_stages, moe_a16w4_forward_noalloc,
   mxfp4_to_int4g32_requant, moe_last_error
 plus two compositions: moe_a16w4_layer (route -> sort -> forward, the
 in-kernel routing path of apply_monolithic on the vLLM mxfp4 API page) and
@@ -36,8 +36,10 @@ MOE_STAGE_GATE_UP, MOE_STAGE_DOWN, MOE_STAGE_COMBINE, MOE_STAGE_ALL = 1, 2, 4, 7
 EXPORTS = (
     "moe_last_error", "moe_route_topk", "moe_align_sort_capacity", "moe_default_block_m",
     "moe_align_sort", "moe_route_align", "moe_a16w4_workspace_size", "moe_a16w4_forward",
-    "moe_a16w4_forward_stages", "mxfp4_to_int4g32_requant",
+    "moe_a16w4_forward_stages", "moe_a16w4_forward_noalloc", "mxfp4_to_int4g32_requant",
 )
+# Scratch of the allocation-free forward (MOE_NOALLOC_SCRATCH_BYTES).
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 class MoeError(RuntimeError):
@@ -72,6 +74,8 @@ def _load():
     L.moe_a16w4_forward_stages.restype = i
     L.moe_a16w4_forward_stages.argtypes = [p, p, p, p, p, i, i, p, p, p, p, p, i, i, i, i, i, i, p, p, sz,
                                            ctypes.c_uint, p]
+    L.moe_a16w4_forward_noalloc.restype = i
+    L.moe_a16w4_forward_noalloc.argtypes = [p, p, p, p, p, i, i, p, p, p, p, p, i, i, i, i, i, i, p, p]
     L.mxfp4_to_int4g32_requant.restype = i
     L.mxfp4_to_int4g32_requant.argtypes = [p, p, i, i, i, i, i, p, p, p]
     return L
@@ -249,6 +253,29 @@ def moe_a16w4_forward(x, w13, w13_scale, w2, w2_scale, topk_ids, topk_weights, s
         _check(lib.moe_a16w4_forward(*args, _stream(stream)))
     else:
         _check(lib.moe_a16w4_forward_stages(*args, int(stages), _stream(stream)))
+    return out
+
+
+def moe_a16w4_forward_noalloc(x, w13, w13_scale, w2, w2_scale, topk_ids, topk_weights, sorted_ids,
+                              block_expert, num_post_pad, block_m, out, fmt=MOE_W_MXFP4,
+                              act=MOE_ACT_SWIGLU, stream=None):
+    """moe_a16w4_forward into a caller-given `out`, with the library's own
+    device scratch as the workspace: neither this function nor the library
+    allocates device memory (for callers that cannot allocate). Calls that
+    overlap in time on one GPU share that scratch and race."""
+    _dev(x, "x", torch.bfloat16, 2)
+    E, H, I = _weights(w13, w13_scale, w2, w2_scale, fmt)
+    T = x.shape[0]
+    if x.shape[1] != H:
+        raise ValueError(f"x has {x.shape[1]} columns, weights expect H={H}")
+    _dev(topk_ids, "topk_ids", torch.int32, 2)
+    _dev(topk_weights, "topk_weights", torch.float32, 2)
+    _dev(out, "out", torch.bfloat16, 2)
+    topk = topk_ids.shape[1]
+    _check(lib.moe_a16w4_forward_noalloc(
+        _ptr(x), _ptr(w13), _ptr(w13_scale), _ptr(w2), _ptr(w2_scale), int(fmt), int(act),
+        _ptr(topk_ids), _ptr(topk_weights), _ptr(sorted_ids), _ptr(block_expert), _ptr(num_post_pad),
+        T, H, I, E, topk, int(block_m), _ptr(out), _stream(stream)))
     return out
 
 

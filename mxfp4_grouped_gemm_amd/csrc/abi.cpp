@@ -8,6 +8,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/moe_a16w4.h"
 #include "launch.hpp"
@@ -298,3 +299,65 @@ moe_status mxfp4_to_int4g32_requant(const uint8_t* w, const uint8_t* scale_e8m0,
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Allocation-free forward: the workspace is a device array of this file
+// (MOE_NOALLOC_SCRATCH_BYTES), loaded with the library's code on each GPU it
+// runs on and kept until the process ends. Host code never passes the
+// array's name to a kernel (on the host it is only a stand-in for the
+// symbol): its device address is looked up once per device, with that device
+// current, and that address is the workspace of every call on the device.
+namespace {
+
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// Device address of `scratch` on the current device (looked up on the first
+// call on that device), or an error status.
+moe_status scratch_on_current_device(void** ptr, const char* fn) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e, fn);
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(MOE_ERR_UNSUPPORTED, "%s: device %d beyond the %d the library tracks", fn, dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_status(e, fn);
+        if (!p || !aligned(p, 256)) return fail(MOE_ERR_HIP, "%s: scratch address %p unusable", fn, p);
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" moe_status moe_a16w4_forward_noalloc(
+    const uint16_t* x, const uint8_t* w13, const void* w13_scale, const uint8_t* w2,
+    const void* w2_scale, moe_wfmt fmt, moe_act act, const int32_t* topk_ids,
+    const float* topk_weights, const int32_t* sorted_ids, const int32_t* block_expert,
+    const int32_t* num_post_pad, int T, int H, int I, int E, int topk, int block_m, uint16_t* out,
+    void* stream) {
+    const char* fn = "moe_a16w4_forward_noalloc";
+    const int64_t need = moe_a16w4_workspace_size(T, H, I, E, topk, block_m);
+    if (need < 0)
+        return fail(MOE_ERR_INVALID_ARG, "%s: invalid sizes T=%d H=%d I=%d E=%d topk=%d block_m=%d", fn,
+                    T, H, I, E, topk, block_m);
+    if (need > (int64_t)MOE_NOALLOC_SCRATCH_BYTES)
+        return fail(MOE_ERR_UNSUPPORTED,
+                    "%s: this batch needs %lld workspace bytes, above the %lld-byte scratch of the "
+                    "allocation-free call; use moe_a16w4_forward with a caller workspace or a smaller batch",
+                    fn, (long long)need, (long long)MOE_NOALLOC_SCRATCH_BYTES);
+    if (T == 0) return MOE_OK;
+    void* ws = nullptr;
+    const moe_status st = scratch_on_current_device(&ws, fn);
+    if (st != MOE_OK) return st;
+    return moe_a16w4_forward(x, w13, w13_scale, w2, w2_scale, fmt, act, topk_ids, topk_weights,
+                             sorted_ids, block_expert, num_post_pad, T, H, I, E, topk, block_m, out, ws,
+                             (size_t)MOE_NOALLOC_SCRATCH_BYTES, stream);
+}
