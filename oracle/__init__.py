@@ -53,6 +53,9 @@ def lib():
         L.oracle_align_sort.argtypes = [p, i, i, i, i, p, p, p, p]
         L.oracle_moe_forward.restype = None
         L.oracle_moe_forward.argtypes = [p, p, p, p, p, i, p, p, i, i, i, i, i, p, i, p]
+        L.oracle_moe_forward_ex.restype = None
+        L.oracle_moe_forward_ex.argtypes = [p, p, p, p, p, p, p, ctypes.c_double, i, p, p, i, i, i, i, i,
+                                            p, i, p]
         L.oracle_requant_int4g32.restype = None
         L.oracle_requant_int4g32.argtypes = [p, p, i, i, i, i, i, p, p]
         L.oracle_num_threads.restype = i
@@ -129,8 +132,10 @@ def align_sort(ids, E: int, bm: int):
 
 
 def moe_forward(x_bf16, w13, w13_scale, w2, w2_scale, fmt, ids, weights,
-                I: int, tokens=None):
-    """out[len(tokens) or T, H] float64. x_bf16 holds bf16 bit patterns."""
+                I: int, tokens=None, w13_bias=None, w2_bias=None, swiglu_limit=0.0):
+    """out[len(tokens) or T, H] float64. x_bf16 holds bf16 bit patterns.
+    w13_bias [E, 2I] / w2_bias [E, H]: optional bf16 bit patterns;
+    swiglu_limit > 0 clamps gate and up to [-limit, limit] before SwiGLU."""
     x = _c(x_bf16, np.uint16)
     T, H = x.shape
     w13 = _c(w13, np.uint8)
@@ -151,10 +156,14 @@ def moe_forward(x_bf16, w13, w13_scale, w2, w2_scale, fmt, ids, weights,
         tok = _c(tokens, np.int32)
         n = tok.size
         assert np.all((tok >= 0) & (tok < T))
+    b13 = None if w13_bias is None else _c(w13_bias, np.uint16)
+    b2 = None if w2_bias is None else _c(w2_bias, np.uint16)
+    assert b13 is None or b13.shape == (E, 2 * I)
+    assert b2 is None or b2.shape == (E, H)
     out = np.empty((n, H), dtype=np.float64)
-    lib().oracle_moe_forward(_ptr(x), _ptr(w13), _ptr(w13s), _ptr(w2), _ptr(w2s), int(fmt),
-                             _ptr(ids), _ptr(weights), T, H, int(I), E, topk,
-                             _ptr(tok), n, _ptr(out))
+    lib().oracle_moe_forward_ex(_ptr(x), _ptr(w13), _ptr(w13s), _ptr(b13), _ptr(w2), _ptr(w2s),
+                                _ptr(b2), float(swiglu_limit), int(fmt), _ptr(ids), _ptr(weights),
+                                T, H, int(I), E, topk, _ptr(tok), n, _ptr(out))
     return out
 
 

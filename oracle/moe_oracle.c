@@ -196,11 +196,20 @@ static double silu(double z) { return z / (1.0 + exp(-z)); }
 
 /* One pair (token t, expert e): gate/up projection against w13 (rows [0, I)
  * gate, rows [I, 2I) up -- the fused gate_up_proj of [P2] create_weights),
- * SwiGLU silu(gate) * up rounded to bf16, then the down projection against
- * w2. y[H] out.
+ * plus the expert's w13 bias when given, each of gate and up clamped to
+ * [-limit, limit] when limit > 0, SwiGLU silu(gate) * up rounded to bf16,
+ * then the down projection against w2 plus the expert's w2 bias when given.
+ * y[H] out.
+ * [P2] create_weights: under has_bias, w13_bias [E, 2I] and w2_bias [E, H]
+ * in bf16; get_fused_moe_quant_config hands them to the kernel with the
+ * layer's swiglu_limit as the GEMM1 clamp limit. The pages do not spell out
+ * where the terms enter; the reading here: each bias is added to its GEMM's
+ * output, the clamp applies to both GEMM1 outputs after the bias and before
+ * the activation.
  * Every dot product is summed in ascending k. */
 static void expert_mlp(const uint16_t* xt, const uint8_t* w13, const void* w13_scale,
                        const uint8_t* w2, const void* w2_scale, int fmt,
+                       const uint16_t* w13_bias, const uint16_t* w2_bias, double limit,
                        int e, int H, int I, double* hbuf, double* y) {
     int64_t r13 = (int64_t)e * 2 * I; /* first w13 row of expert e */
     int64_t r2 = (int64_t)e * H;      /* first w2 row of expert e */
@@ -219,6 +228,14 @@ static void expert_mlp(const uint16_t* xt, const uint8_t* w13, const void* w13_s
                 g += wg[k] * xv[k];
                 u += wu[k] * xv[k];
             }
+            if (w13_bias) {
+                g += oracle_bf16_value(w13_bias[(int64_t)e * 2 * I + i]);
+                u += oracle_bf16_value(w13_bias[(int64_t)e * 2 * I + I + i]);
+            }
+            if (limit > 0.0) {
+                g = g > limit ? limit : (g < -limit ? -limit : g);
+                u = u > limit ? limit : (u < -limit ? -limit : u);
+            }
             /* A16W4: both grouped GEMMs take bf16 activations, so the
              * SwiGLU output enters the down projection as bf16 ([P1]
              * Summary: the BF16 x packed-int4 path; [P2] EMULATION comment:
@@ -236,6 +253,7 @@ static void expert_mlp(const uint16_t* xt, const uint8_t* w13, const void* w13_s
             dequant_row(w2, w2_scale, fmt, I, r2 + n, wd);
             double acc = 0.0;
             for (int i = 0; i < I; ++i) acc += wd[i] * hbuf[i];
+            if (w2_bias) acc += oracle_bf16_value(w2_bias[(int64_t)e * H + n]);
             y[n] = acc;
         }
         free(wd);
@@ -248,11 +266,12 @@ static void expert_mlp(const uint16_t* xt, const uint8_t* w13, const void* w13_s
  * apply() in [P2] (apply_router_weight_on_input off). W4A16: bf16
  * activations, weights dequantized ([P2] get_fused_moe_quant_config, the
  * EMULATION comment). */
-void oracle_moe_forward(const uint16_t* x, const uint8_t* w13, const void* w13_scale,
-                        const uint8_t* w2, const void* w2_scale, int fmt,
-                        const int32_t* ids, const float* weights,
-                        int T, int H, int I, int E, int topk,
-                        const int32_t* tokens, int n_tokens, double* out) {
+void oracle_moe_forward_ex(const uint16_t* x, const uint8_t* w13, const void* w13_scale,
+                           const uint16_t* w13_bias, const uint8_t* w2, const void* w2_scale,
+                           const uint16_t* w2_bias, double swiglu_limit, int fmt,
+                           const int32_t* ids, const float* weights,
+                           int T, int H, int I, int E, int topk,
+                           const int32_t* tokens, int n_tokens, double* out) {
     double* hbuf = (double*)malloc(sizeof(double) * (size_t)I);
     double* y = (double*)malloc(sizeof(double) * (size_t)H);
     int count = tokens ? n_tokens : T;
@@ -264,13 +283,22 @@ void oracle_moe_forward(const uint16_t* x, const uint8_t* w13, const void* w13_s
             int e = ids[(int64_t)t * topk + j];
             if (e < 0 || e >= E) continue;
             expert_mlp(x + (int64_t)t * H, w13, w13_scale, w2, w2_scale, fmt,
-                       e, H, I, hbuf, y);
+                       w13_bias, w2_bias, swiglu_limit, e, H, I, hbuf, y);
             double wj = (double)weights[(int64_t)t * topk + j];
             for (int n = 0; n < H; ++n) o[n] += wj * y[n];
         }
     }
     free(y);
     free(hbuf);
+}
+
+void oracle_moe_forward(const uint16_t* x, const uint8_t* w13, const void* w13_scale,
+                        const uint8_t* w2, const void* w2_scale, int fmt,
+                        const int32_t* ids, const float* weights,
+                        int T, int H, int I, int E, int topk,
+                        const int32_t* tokens, int n_tokens, double* out) {
+    oracle_moe_forward_ex(x, w13, w13_scale, NULL, w2, w2_scale, NULL, 0.0, fmt, ids, weights,
+                          T, H, I, E, topk, tokens, n_tokens, out);
 }
 
 /* --------------------------------------------------------------- requant -- */

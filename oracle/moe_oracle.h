@@ -73,6 +73,17 @@ void oracle_moe_forward(const uint16_t* x, const uint8_t* w13, const void* w13_s
                         int T, int H, int I, int E, int topk,
                         const int32_t* tokens, int n_tokens, double* out);
 
+/* The same with the optional expert biases and GEMM1 clamp:
+ * w13_bias bf16 [E, 2I] (gate biases, then up biases) and w2_bias bf16
+ * [E, H], each NULL for none; swiglu_limit > 0 clamps gate and up (after
+ * their bias) to [-limit, limit] before SwiGLU, <= 0 leaves them. */
+void oracle_moe_forward_ex(const uint16_t* x, const uint8_t* w13, const void* w13_scale,
+                           const uint16_t* w13_bias, const uint8_t* w2, const void* w2_scale,
+                           const uint16_t* w2_bias, double swiglu_limit, int fmt,
+                           const int32_t* ids, const float* weights,
+                           int T, int H, int I, int E, int topk,
+                           const int32_t* tokens, int n_tokens, double* out);
+
 /* MXFP4 -> int4 per-group-32 requantisation of experts [lo, hi) of a
  * [E, N, K] weight. Outputs are full-size [E, N, K/2] codes and
  * [E, N, K/32] bf16 scales; only the experts in [lo, hi) are written. */

@@ -110,6 +110,18 @@ def make(spec: Spec, T: Optional[int] = None, with_weights: bool = True) -> Work
     return Workload(s, logits, x, w13, w13_scale, w2, w2_scale, hot)
 
 
+def biases(E: int, H: int, I: int, seed: int, scale13: float = 64.0, scale2: float = 2.0 ** 19):
+    """Expert biases as bf16 bit patterns (create_weights under has_bias):
+    w13_bias [E, 2I] ~ N(0, scale13^2) and w2_bias [E, H] ~ N(0, scale2^2),
+    drawn in that order from Generator(PCG64(seed)). The default scales
+    are of the order of the GEMM outputs at the workloads' value
+    distributions, so the biases change the results visibly."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    b13 = to_bf16_bits(rng.standard_normal((E, 2 * I), dtype=np.float32) * np.float32(scale13))
+    b2 = to_bf16_bits(rng.standard_normal((E, H), dtype=np.float32) * np.float32(scale2))
+    return b13, b2
+
+
 def small(T, H, I, E, topk, seed, scale_lo=120, scale_hi=130, hot=0) -> Workload:
     """An ad-hoc small workload with the same distributions."""
     return make(Spec("adhoc", T=T, H=H, I=I, E=E, topk=topk, seed=seed,
