@@ -180,6 +180,31 @@ moe_status moe_a16w4_forward_stages(const uint16_t* x, const uint8_t* w13, const
                                     void* workspace, size_t workspace_bytes, unsigned stages,
                                     void* stream);
 
+/* moe_a16w4_forward_stages with the optional expert biases and GEMM1 clamp
+ * of the mxfp4 API page (create_weights under has_bias makes w13_bias and
+ * w2_bias in bf16; get_fused_moe_quant_config passes them to the kernel with
+ * the layer's swiglu_limit as the GEMM1 clamp limit):
+ *   gate/up = W13[e] . x + w13_bias[e]   (w13_bias bf16 [E, 2I]: gate biases
+ *                                          in [0, I), up biases in [I, 2I))
+ *   gate, up clamped to [-swiglu_limit, swiglu_limit] when swiglu_limit > 0
+ *   h = silu(gate) * up;  y = W2[e] . h + w2_bias[e]  (w2_bias bf16 [E, H])
+ *   out[t] = sum_j weight[t, j] * y(t, j).
+ * The pages name these terms but print no formula; this placement (each
+ * bias on its GEMM's output, the clamp on both GEMM1 outputs before the
+ * activation) is the reading taken. Either bias may be NULL (no term);
+ * swiglu_limit == 0 means no clamp, a negative or NaN limit is
+ * MOE_ERR_INVALID_ARG. Bias pointers 16-byte aligned. Everything else as
+ * moe_a16w4_forward_stages; the w2 bias is applied by the combine stage. */
+moe_status moe_a16w4_forward_ex(const uint16_t* x, const uint8_t* w13, const void* w13_scale,
+                                const uint16_t* w13_bias, const uint8_t* w2, const void* w2_scale,
+                                const uint16_t* w2_bias, moe_wfmt fmt, moe_act act,
+                                float swiglu_limit, const int32_t* topk_ids,
+                                const float* topk_weights, const int32_t* sorted_ids,
+                                const int32_t* block_expert, const int32_t* num_post_pad, int T,
+                                int H, int I, int E, int topk, int block_m, uint16_t* out,
+                                void* workspace, size_t workspace_bytes, unsigned stages,
+                                void* stream);
+
 /* moe_a16w4_forward without a workspace argument, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving
  * loops, harnesses that forbid hipMalloc). The workspace is the library's

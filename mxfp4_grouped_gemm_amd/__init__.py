@@ -10,7 +10,7 @@ library has not been built.
 Functions mirror the C ABI names:
   moe_route_topk, moe_align_sort_capacity, moe_default_block_m,
   moe_align_sort, moe_route_align, moe_a16w4_workspace_size, moe_a16w4_forward,
-  moe_a16w4_forward_stages, moe_a16w4_forward_noalloc,
+  moe_a16w4_forward_stages, moe_a16w4_forward_ex, moe_a16w4_forward_noalloc,
   mxfp4_to_int4g32_requant, moe_last_error
 plus two compositions: moe_a16w4_layer (route -> sort -> forward, the
 in-kernel routing path of apply_monolithic on the vLLM mxfp4 API page) and
@@ -36,7 +36,8 @@ MOE_STAGE_GATE_UP, MOE_STAGE_DOWN, MOE_STAGE_COMBINE, MOE_STAGE_ALL = 1, 2, 4, 7
 EXPORTS = (
     "moe_last_error", "moe_route_topk", "moe_align_sort_capacity", "moe_default_block_m",
     "moe_align_sort", "moe_route_align", "moe_a16w4_workspace_size", "moe_a16w4_forward",
-    "moe_a16w4_forward_stages", "moe_a16w4_forward_noalloc", "mxfp4_to_int4g32_requant",
+    "moe_a16w4_forward_stages", "moe_a16w4_forward_ex", "moe_a16w4_forward_noalloc",
+    "mxfp4_to_int4g32_requant",
 )
 # Scratch of the allocation-free forward (MOE_NOALLOC_SCRATCH_BYTES).
 NOALLOC_SCRATCH_BYTES = 64 << 20
@@ -74,6 +75,9 @@ def _load():
     L.moe_a16w4_forward_stages.restype = i
     L.moe_a16w4_forward_stages.argtypes = [p, p, p, p, p, i, i, p, p, p, p, p, i, i, i, i, i, i, p, p, sz,
                                            ctypes.c_uint, p]
+    L.moe_a16w4_forward_ex.restype = i
+    L.moe_a16w4_forward_ex.argtypes = [p, p, p, p, p, p, p, i, i, ctypes.c_float, p, p, p, p, p, i, i, i, i,
+                                       i, i, p, p, sz, ctypes.c_uint, p]
     L.moe_a16w4_forward_noalloc.restype = i
     L.moe_a16w4_forward_noalloc.argtypes = [p, p, p, p, p, i, i, p, p, p, p, p, i, i, i, i, i, i, p, p]
     L.mxfp4_to_int4g32_requant.restype = i
@@ -223,11 +227,24 @@ def _weights(w13, w13_scale, w2, w2_scale, fmt):
     return E, H, I
 
 
+def _bias(b, name, shape):
+    if b is None:
+        return None
+    _dev(b, name, (torch.bfloat16, torch.int16, torch.uint16), 2)
+    if tuple(b.shape) != shape:
+        raise ValueError(f"{name} must have shape {shape}, got {tuple(b.shape)}")
+    return b
+
+
 def moe_a16w4_forward(x, w13, w13_scale, w2, w2_scale, topk_ids, topk_weights, sorted_ids,
                       block_expert, num_post_pad, block_m, fmt=MOE_W_MXFP4, act=MOE_ACT_SWIGLU,
-                      out=None, workspace=None, stream=None, stages=MOE_STAGE_ALL):
+                      out=None, workspace=None, stream=None, stages=MOE_STAGE_ALL,
+                      w13_bias=None, w2_bias=None, swiglu_limit=0.0):
     """Fused MoE forward with precomputed routing. x bf16 [T, H] -> out bf16 [T, H].
-    `stages` selects a subset of the launches (moe_a16w4_forward_stages)."""
+    `stages` selects a subset of the launches (moe_a16w4_forward_stages).
+    Optional expert biases w13_bias bf16 [E, 2I] and w2_bias bf16 [E, H], and
+    swiglu_limit > 0 clamping gate and up to [-limit, limit]
+    (moe_a16w4_forward_ex)."""
     _dev(x, "x", torch.bfloat16, 2)
     E, H, I = _weights(w13, w13_scale, w2, w2_scale, fmt)
     T = x.shape[0]
@@ -245,6 +262,15 @@ def moe_a16w4_forward(x, w13, w13_scale, w2, w2_scale, topk_ids, topk_weights, s
         if workspace is None:
             workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=x.device)
     _dev(out, "out", torch.bfloat16)
+    _bias(w13_bias, "w13_bias", (E, 2 * I))
+    _bias(w2_bias, "w2_bias", (E, H))
+    if w13_bias is not None or w2_bias is not None or swiglu_limit:
+        _check(lib.moe_a16w4_forward_ex(
+            _ptr(x), _ptr(w13), _ptr(w13_scale), _ptr(w13_bias), _ptr(w2), _ptr(w2_scale), _ptr(w2_bias),
+            int(fmt), int(act), float(swiglu_limit), _ptr(topk_ids), _ptr(topk_weights), _ptr(sorted_ids),
+            _ptr(block_expert), _ptr(num_post_pad), T, H, I, E, topk, int(block_m), _ptr(out),
+            _ptr(workspace), workspace.numel(), int(stages), _stream(stream)))
+        return out
     args = (_ptr(x), _ptr(w13), _ptr(w13_scale), _ptr(w2), _ptr(w2_scale), int(fmt), int(act),
             _ptr(topk_ids), _ptr(topk_weights), _ptr(sorted_ids), _ptr(block_expert),
             _ptr(num_post_pad), T, H, I, E, topk, int(block_m), _ptr(out), _ptr(workspace),
@@ -280,7 +306,8 @@ def moe_a16w4_forward_noalloc(x, w13, w13_scale, w2, w2_scale, topk_ids, topk_we
 
 
 def moe_a16w4_layer(x, router_logits, w13, w13_scale, w2, w2_scale, topk, fmt=MOE_W_MXFP4,
-                    renormalize=True, block_m=None, stream=None):
+                    renormalize=True, block_m=None, stream=None, w13_bias=None, w2_bias=None,
+                    swiglu_limit=0.0):
     """route -> align/sort -> forward on one stream (no host synchronisation).
     With an explicit `stream` every tensor the call creates is allocated on
     that stream (the routing and sort arrays, the workspace and the output),
@@ -292,7 +319,8 @@ def moe_a16w4_layer(x, router_logits, w13, w13_scale, w2, w2_scale, topk, fmt=MO
     ids, w, sorted_ids, block_expert, _, npp = moe_route_align(router_logits, topk, E, bm, renormalize,
                                                               stream=stream)
     return moe_a16w4_forward(x, w13, w13_scale, w2, w2_scale, ids, w, sorted_ids, block_expert, npp,
-                             bm, fmt=fmt, stream=stream)
+                             bm, fmt=fmt, stream=stream, w13_bias=w13_bias, w2_bias=w2_bias,
+                             swiglu_limit=swiglu_limit)
 
 
 def mxfp4_to_int4g32_requant(w, scale_e8m0, expert_lo, expert_hi, w_int4, scale_bf16, stream=None):

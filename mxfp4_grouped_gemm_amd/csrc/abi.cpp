@@ -189,9 +189,26 @@ moe_status moe_a16w4_forward_stages(const uint16_t* x, const uint8_t* w13, const
                                     int H, int I, int E, int topk, int block_m, uint16_t* out,
                                     void* workspace, size_t workspace_bytes, unsigned stages,
                                     void* stream) {
+    return moe_a16w4_forward_ex(x, w13, w13_scale, nullptr, w2, w2_scale, nullptr, fmt, act, 0.0f,
+                                topk_ids, topk_weights, sorted_ids, block_expert, num_post_pad, T, H,
+                                I, E, topk, block_m, out, workspace, workspace_bytes, stages, stream);
+}
+
+moe_status moe_a16w4_forward_ex(const uint16_t* x, const uint8_t* w13, const void* w13_scale,
+                                const uint16_t* w13_bias, const uint8_t* w2, const void* w2_scale,
+                                const uint16_t* w2_bias, moe_wfmt fmt, moe_act act,
+                                float swiglu_limit, const int32_t* topk_ids,
+                                const float* topk_weights, const int32_t* sorted_ids,
+                                const int32_t* block_expert, const int32_t* num_post_pad, int T,
+                                int H, int I, int E, int topk, int block_m, uint16_t* out,
+                                void* workspace, size_t workspace_bytes, unsigned stages,
+                                void* stream) {
     const char* fn = "moe_a16w4_forward";
     if (stages == 0 || (stages & ~MOE_STAGE_ALL))
         return fail(MOE_ERR_INVALID_ARG, "%s: stage mask 0x%x invalid", fn, stages);
+    if (!(swiglu_limit >= 0.0f))
+        return fail(MOE_ERR_INVALID_ARG, "%s: swiglu_limit %g must be >= 0 (0 = no clamp)", fn,
+                    (double)swiglu_limit);
     if (act != MOE_ACT_SWIGLU)
         return fail(MOE_ERR_UNSUPPORTED, "%s: activation %d is not implemented (only SwiGLU); "
                     "refusing to compute a different activation", fn, (int)act);
@@ -227,6 +244,8 @@ moe_status moe_a16w4_forward_stages(const uint16_t* x, const uint8_t* w13, const
     for (const void* p : ptrs)
         if (!aligned(p, 16)) return fail(MOE_ERR_INVALID_ARG, "%s: pointer %p not 16-byte aligned", fn, p);
     if (!aligned(workspace, 256)) return fail(MOE_ERR_INVALID_ARG, "%s: workspace not 256-byte aligned", fn);
+    if (!aligned(w13_bias, 16) || !aligned(w2_bias, 16))
+        return fail(MOE_ERR_INVALID_ARG, "%s: bias pointers must be 16-byte aligned", fn);
     const WsLayout L = ws_layout(T, H, I, E, topk, block_m);
     if ((int64_t)workspace_bytes < L.total)
         return fail(MOE_ERR_INVALID_ARG, "%s: workspace %zu bytes < %lld needed", fn, workspace_bytes,
@@ -254,6 +273,9 @@ moe_status moe_a16w4_forward_stages(const uint16_t* x, const uint8_t* w13, const
     a.topk_ids = topk_ids;
     a.topk_weights = topk_weights;
     a.out = out;
+    a.w13_bias = w13_bias;
+    a.w2_bias = w2_bias;
+    a.swiglu_limit = swiglu_limit;
     hipStream_t s = (hipStream_t)stream;
     moe_status st = MOE_OK;
     // Kernel family per shape: GEMV waves for blocks of <= 8 token rows,
@@ -276,7 +298,7 @@ moe_status moe_a16w4_forward_stages(const uint16_t* x, const uint8_t* w13, const
         if (st != MOE_OK) return st;
     }
     if (stages & MOE_STAGE_COMBINE)
-        st = hip_status(moe::launch_combine(a.y, topk_ids, topk_weights, T, H, E, topk, out, s),
+        st = hip_status(moe::launch_combine(a.y, topk_ids, topk_weights, w2_bias, T, H, E, topk, out, s),
                         "moe_a16w4_forward (combine)");
     return st;
 }

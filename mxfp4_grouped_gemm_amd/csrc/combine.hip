@@ -1,7 +1,9 @@
 // Top-k weighted combine: out[t] = sum over slots j (ascending) of
 // weight[t, j] * y[t*topk + j], fp32 accumulation, bf16 output. The router
 // weight is applied here, after the expert MLP -- the default of apply() on
-// the vLLM mxfp4 API page (apply_router_weight_on_input off).
+// the vLLM mxfp4 API page (apply_router_weight_on_input off). With expert
+// biases (create_weights under has_bias) the slot's w2 bias row joins its
+// y row here: weight * (y + w2_bias[expert]).
 //
 // One thread per 4 output columns. For topk <= 16 a workgroup owns 1024
 // columns of one token and all slot rows are fetched at once with branch-
@@ -13,10 +15,11 @@
 
 namespace moe {
 
-template <int KMAX>
+template <int KMAX, bool BIAS>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y,
                                                       const int32_t* __restrict__ ids,
-                                                      const float* __restrict__ weights, int T,
+                                                      const float* __restrict__ weights,
+                                                      const uint16_t* __restrict__ w2_bias, int T,
                                                       int H, int E, int topk,
                                                       uint16_t* __restrict__ out) {
     // Workgroup = (token t, 1024 columns).
@@ -42,6 +45,18 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
         const uint32_t off = (j < topk && n < H) ? (uint32_t)(((p0 + j) * H + n) * 4) : kOob;
         v[j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ry, off, 0, kNt));
     }
+    // Bias rows of the slots' experts (4 bf16 per lane and slot): their
+    // addresses need the ids, so they follow the y loads.
+    u32x2 bv[KMAX];
+    if constexpr (BIAS) {
+        const rsrc_t rb = make_rsrc(w2_bias, (uint32_t)((int64_t)E * H * 2));
+#pragma unroll
+        for (int j = 0; j < KMAX; ++j) {
+            const int e = __builtin_amdgcn_readlane(id_l, j);
+            const bool ok = j < topk && n < H && (unsigned)e < (unsigned)E;
+            bv[j] = bld8(rb, ok ? ((uint32_t)e * (uint32_t)H + (uint32_t)n) * 2u : kOob);
+        }
+    }
     if (n >= H) return;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
@@ -50,8 +65,14 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
         const int e = __builtin_amdgcn_readlane(id_l, j);
         const float wj = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w_l), j));
         const bool ok = j < topk && (unsigned)e < (unsigned)E;
-        const f32x4 vj = ok ? v[j] : zero;
+        f32x4 vj = ok ? v[j] : zero;
         const float w = ok ? wj : 0.0f;
+        if constexpr (BIAS) {
+            vj[0] += __uint_as_float(bv[j][0] << 16);
+            vj[1] += __uint_as_float(bv[j][0] & 0xffff0000u);
+            vj[2] += __uint_as_float(bv[j][1] << 16);
+            vj[3] += __uint_as_float(bv[j][1] & 0xffff0000u);
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc[i] = fmaf(w, vj[i], acc[i]);
     }
@@ -65,6 +86,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 __global__ __launch_bounds__(256) void combine_loop_kernel(const float* __restrict__ y,
                                                            const int32_t* __restrict__ ids,
                                                            const float* __restrict__ weights,
+                                                           const uint16_t* __restrict__ w2_bias,
                                                            int T, int H, int E, int topk,
                                                            uint16_t* __restrict__ out) {
     const int cpr = H / 4;
@@ -78,7 +100,12 @@ __global__ __launch_bounds__(256) void combine_loop_kernel(const float* __restri
         const int e = ids[p];
         if ((unsigned)e >= (unsigned)E) continue;
         const float wv = weights[p];
-        const f32x4 v = *(const f32x4*)(y + p * H + n);
+        f32x4 v = *(const f32x4*)(y + p * H + n);
+        if (w2_bias) {
+            const uint16_t* b = w2_bias + (int64_t)e * H + n;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v[i] += __uint_as_float((uint32_t)b[i] << 16);
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc[i] = fmaf(wv, v[i], acc[i]);
     }
@@ -88,16 +115,23 @@ __global__ __launch_bounds__(256) void combine_loop_kernel(const float* __restri
     *(u32x2*)(out + (int64_t)t * H + n) = o;
 }
 
-hipError_t launch_combine(const float* y, const int32_t* ids, const float* weights, int T, int H,
-                          int E, int topk, uint16_t* out, hipStream_t s) {
+hipError_t launch_combine(const float* y, const int32_t* ids, const float* weights,
+                          const uint16_t* w2_bias, int T, int H, int E, int topk, uint16_t* out,
+                          hipStream_t s) {
     const int64_t ybytes = (int64_t)T * topk * H * 4;
     if (topk <= 16 && ybytes < 0x7fff0000LL) {
         const dim3 grid((unsigned)((int64_t)T * ((H + 1023) / 1024))), block(256);
-        hipLaunchKernelGGL(combine_kernel<16>, grid, block, 0, s, y, ids, weights, T, H, E, topk, out);
+        if (w2_bias)
+            hipLaunchKernelGGL((combine_kernel<16, true>), grid, block, 0, s, y, ids, weights, w2_bias, T, H,
+                               E, topk, out);
+        else
+            hipLaunchKernelGGL((combine_kernel<16, false>), grid, block, 0, s, y, ids, weights, w2_bias, T,
+                               H, E, topk, out);
     } else {
         const int64_t threads = (int64_t)T * (H / 4);
         const dim3 grid((unsigned)((threads + 255) / 256)), block(256);
-        hipLaunchKernelGGL(combine_loop_kernel, grid, block, 0, s, y, ids, weights, T, H, E, topk, out);
+        hipLaunchKernelGGL(combine_loop_kernel, grid, block, 0, s, y, ids, weights, w2_bias, T, H, E, topk,
+                           out);
     }
     return hipGetLastError();
 }

@@ -207,14 +207,19 @@ __global__ __launch_bounds__(kUnitWaves * 64) void stage1_unit_kernel(MoeGemmArg
     unit_k_loop<FMT, MSUB>(o, nact, H, g, accg, accu);
 
     // C layout: this lane holds rows 4g + j, column nl.
+    GluTerms glu;
+    glu.load(a, e, i0 + nl);
 #pragma unroll
     for (int s = 0; s < MSUB; ++s) {
         if (s >= nact) break;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int m = 4 * g + j;
-            if (m < valid[s])
-                a.h[(row0 + 16 * s + m) * I + i0 + nl] = f32_to_bf16_bits(swiglu(accg[s][j], accu[s][j]));
+            if (m < valid[s]) {
+                float gv = accg[s][j], uv = accu[s][j];
+                glu.apply(gv, uv);
+                a.h[(row0 + 16 * s + m) * I + i0 + nl] = f32_to_bf16_bits(swiglu(gv, uv));
+            }
         }
     }
 }

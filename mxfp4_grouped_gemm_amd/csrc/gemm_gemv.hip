@@ -155,7 +155,9 @@ __device__ __forceinline__ void gemv_dot(const GemvWeights<NCH>& W, const uint8_
 // per SIMD keep about 1.5x more weight bytes in flight per CU than the
 // compiler's default of four (35 -> 32 us at the production decode shape).
 // With rows reloaded in sequence the default allocation is faster.
-template <int NR, int NRMAX, int NCH>
+// EPI: with the optional expert bias / clamp epilogue (instances launched
+// without them are built without it, so their registers are untouched).
+template <int NR, int NRMAX, int NCH, bool EPI>
 __global__ __launch_bounds__(kGemvWaves1 * 64) __attribute__((amdgpu_waves_per_eu(NRMAX == 1 ? 6 : 1)))
 void stage1_gemv_kernel(MoeGemmArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t lds_scale[kGemvWaves1][4 * 64 * NCH];
@@ -178,6 +180,15 @@ void stage1_gemv_kernel(MoeGemmArgs a) {
     if (e < 0 || e >= a.E) return;
     const int i0 = (int)(u % upb) * 2;
     const int H = a.H, I = a.I, nblk = H / 32;
+    // The unit's gate and up biases (columns i0, i0 + 1: one aligned dword
+    // each), read with wave-uniform loads before anything is stored, so they
+    // sit in scalar registers and cost the weight stream no VGPRs.
+    uint32_t bgate = 0u, bup = 0u;
+    if (EPI && a.w13_bias) {
+        const uint16_t* bb = a.w13_bias + (int64_t)e * 2 * I + i0;
+        bgate = __builtin_amdgcn_readfirstlane(*(const uint32_t*)bb);
+        bup = __builtin_amdgcn_readfirstlane(*(const uint32_t*)(bb + I));
+    }
 
     const int64_t slab_rows = 2 * (int64_t)I;
     const rsrc_t rw = make_rsrc(a.w13 + e * slab_rows * (H / 2), (uint32_t)(slab_rows * (H / 2)));
@@ -208,8 +219,20 @@ void stage1_gemv_kernel(MoeGemmArgs a) {
         float v[4] = {acc[0], acc[2], acc[1], acc[3]};
         float gs = reduce4(v), us = gs;
         permlane32_swap(gs, us);
-        if ((lane & 15) == 0 && lane < 32)
+        if ((lane & 15) == 0 && lane < 32) {
+            if constexpr (EPI) {
+                if (a.w13_bias) {  // lane 0 takes column i0 (low halves), lane 16 column i0 + 1
+                    gs += __uint_as_float(lane ? (bgate & 0xffff0000u) : (bgate << 16));
+                    us += __uint_as_float(lane ? (bup & 0xffff0000u) : (bup << 16));
+                }
+                const float lim = a.swiglu_limit;
+                if (lim > 0.0f) {
+                    gs = fminf(fmaxf(gs, -lim), lim);
+                    us = fminf(fmaxf(us, -lim), lim);
+                }
+            }
             a.h[(int64_t)pair[m] * I + i0 + (lane >> 4)] = f32_to_bf16_bits(swiglu(gs, us));
+        }
     }
 }
 
@@ -340,8 +363,14 @@ template <int NRMAX>
 static void launch_stage1_nr(const MoeGemmArgs& a, int nch, hipStream_t s) {
     const int64_t units = (a.cap / a.bm) * (a.I / 2);
     const dim3 grid((unsigned)((units + kGemvWaves1 - 1) / kGemvWaves1)), block(kGemvWaves1 * 64);
-    if (nch == 1) hipLaunchKernelGGL((stage1_gemv_kernel<1, NRMAX, 1>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((stage1_gemv_kernel<1, NRMAX, 2>), grid, block, 0, s, a);
+    const bool epi = a.w13_bias || a.swiglu_limit > 0.0f;
+    if (nch == 1) {
+        if (epi) hipLaunchKernelGGL((stage1_gemv_kernel<1, NRMAX, 1, true>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((stage1_gemv_kernel<1, NRMAX, 1, false>), grid, block, 0, s, a);
+    } else {
+        if (epi) hipLaunchKernelGGL((stage1_gemv_kernel<1, NRMAX, 2, true>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((stage1_gemv_kernel<1, NRMAX, 2, false>), grid, block, 0, s, a);
+    }
 }
 
 template <int NHC>

@@ -66,7 +66,8 @@ __global__ __launch_bounds__(1024) void superblock_kernel(const int32_t* __restr
     if (tid == 0) *count = carry_cnt;
 }
 
-template <int STAGE, int FMT, int NBMAX>
+// EPI: stage 1 with the optional expert-bias / clamp epilogue.
+template <int STAGE, int FMT, int NBMAX, bool EPI>
 __global__ __launch_bounds__(kPfThreads, NBMAX <= 2 ? 2 : 1) void prefill_kernel(MoeGemmArgs a,
                                                                                const int4* __restrict__ list,
                                                                                const int* __restrict__ count,
@@ -86,18 +87,18 @@ __global__ __launch_bounds__(kPfThreads, NBMAX <= 2 ? 2 : 1) void prefill_kernel
     __syncthreads();
     const int n0 = nt * (STAGE == 1 ? 128 : 256);
     if constexpr (NBMAX <= 2) {
-        if (nb == 1) pf_tile<STAGE, FMT, 1, false>(a, sh, e, row0, n0);
-        else pf_tile<STAGE, FMT, 2, false>(a, sh, e, row0, n0);
+        if (nb == 1) pf_tile<STAGE, FMT, 1, false, PfShared<NBMAX>, EPI>(a, sh, e, row0, n0);
+        else pf_tile<STAGE, FMT, 2, false, PfShared<NBMAX>, EPI>(a, sh, e, row0, n0);
     } else {
         switch (nb) {
-            case 1: pf_tile<STAGE, FMT, 1, false>(a, sh, e, row0, n0); break;
-            case 2: pf_tile<STAGE, FMT, 2, false>(a, sh, e, row0, n0); break;
-            case 3: pf_tile<STAGE, FMT, 3, false>(a, sh, e, row0, n0); break;
-            case 4: pf_tile<STAGE, FMT, 4, false>(a, sh, e, row0, n0); break;
-            case 5: pf_tile<STAGE, FMT, 5, false>(a, sh, e, row0, n0); break;
-            case 6: pf_tile<STAGE, FMT, 6, false>(a, sh, e, row0, n0); break;
-            case 7: pf_tile<STAGE, FMT, 7, false>(a, sh, e, row0, n0); break;
-            default: pf_tile<STAGE, FMT, 8, false>(a, sh, e, row0, n0); break;
+            case 1: pf_tile<STAGE, FMT, 1, false, PfShared<NBMAX>, EPI>(a, sh, e, row0, n0); break;
+            case 2: pf_tile<STAGE, FMT, 2, false, PfShared<NBMAX>, EPI>(a, sh, e, row0, n0); break;
+            case 3: pf_tile<STAGE, FMT, 3, false, PfShared<NBMAX>, EPI>(a, sh, e, row0, n0); break;
+            case 4: pf_tile<STAGE, FMT, 4, false, PfShared<NBMAX>, EPI>(a, sh, e, row0, n0); break;
+            case 5: pf_tile<STAGE, FMT, 5, false, PfShared<NBMAX>, EPI>(a, sh, e, row0, n0); break;
+            case 6: pf_tile<STAGE, FMT, 6, false, PfShared<NBMAX>, EPI>(a, sh, e, row0, n0); break;
+            case 7: pf_tile<STAGE, FMT, 7, false, PfShared<NBMAX>, EPI>(a, sh, e, row0, n0); break;
+            default: pf_tile<STAGE, FMT, 8, false, PfShared<NBMAX>, EPI>(a, sh, e, row0, n0); break;
         }
     }
 }
@@ -143,19 +144,22 @@ hipError_t launch_prefill(const MoeGemmArgs& a, int stage, void* list_ws, hipStr
     if (sbound > nblocks) sbound = nblocks;
     const int ntiles = stage == 1 ? a.I / 128 : a.H / 256;
     const int64_t grid = 8 * ((sbound + 7) / 8) * ntiles;
-#define MOE_PF_LAUNCH(ST, F, NBM) \
-    hipLaunchKernelGGL((prefill_kernel<ST, F, NBM>), dim3((unsigned)grid), dim3(kPfThreads), 0, s, a, list, count, ntiles)
-#define MOE_PF_LAUNCH_F(ST, NBM)                                   \
-    do {                                                           \
-        if (a.fmt == kFmtMxfp4) MOE_PF_LAUNCH(ST, kFmtMxfp4, NBM); \
-        else MOE_PF_LAUNCH(ST, kFmtInt4g32, NBM);                 \
+    const bool epi = stage == 1 && (a.w13_bias || a.swiglu_limit > 0.0f);
+#define MOE_PF_LAUNCH(ST, F, NBM, EP) \
+    hipLaunchKernelGGL((prefill_kernel<ST, F, NBM, EP>), dim3((unsigned)grid), dim3(kPfThreads), 0, s, a, list, count, ntiles)
+#define MOE_PF_LAUNCH_F(ST, NBM, EP)                                   \
+    do {                                                               \
+        if (a.fmt == kFmtMxfp4) MOE_PF_LAUNCH(ST, kFmtMxfp4, NBM, EP); \
+        else MOE_PF_LAUNCH(ST, kFmtInt4g32, NBM, EP);                 \
     } while (0)
     if (maxb == kPfMaxBlocksSmall) {
-        if (stage == 1) MOE_PF_LAUNCH_F(1, kPfMaxBlocksSmall);
-        else MOE_PF_LAUNCH_F(2, kPfMaxBlocksSmall);
+        if (stage == 2) MOE_PF_LAUNCH_F(2, kPfMaxBlocksSmall, false);
+        else if (epi) MOE_PF_LAUNCH_F(1, kPfMaxBlocksSmall, true);
+        else MOE_PF_LAUNCH_F(1, kPfMaxBlocksSmall, false);
     } else {
-        if (stage == 1) MOE_PF_LAUNCH_F(1, kPfMaxBlocks);
-        else MOE_PF_LAUNCH_F(2, kPfMaxBlocks);
+        if (stage == 2) MOE_PF_LAUNCH_F(2, kPfMaxBlocks, false);
+        else if (epi) MOE_PF_LAUNCH_F(1, kPfMaxBlocks, true);
+        else MOE_PF_LAUNCH_F(1, kPfMaxBlocks, false);
     }
 #undef MOE_PF_LAUNCH_F
 #undef MOE_PF_LAUNCH

@@ -185,6 +185,8 @@ __global__ __launch_bounds__(kStreamThreads) void stage1_stream_kernel(MoeGemmAr
     }
     __syncthreads();
     const int row = tid >> 4, col = tid & 15;
+    GluTerms glu;
+    glu.load(a, e, i0 + col);
     for (int s = 0; s < nact; ++s) {
         const int64_t r = row0 + 16 * s + row;
         const int p = a.sorted_ids[r];
@@ -195,6 +197,7 @@ __global__ __launch_bounds__(kStreamThreads) void stage1_stream_kernel(MoeGemmAr
             gs += red[w][s][0][row][col];
             us += red[w][s][1][row][col];
         }
+        glu.apply(gs, us);
         a.h[r * I + i0 + col] = f32_to_bf16_bits(swiglu(gs, us));
     }
 }

@@ -37,9 +37,39 @@ struct MoeGemmArgs {
     const int32_t* topk_ids;     // [T, topk]
     const float* topk_weights;   // [T, topk]
     uint16_t* out;               // bf16 [T, H]
+    const uint16_t* w13_bias;    // bf16 [E, 2I] (gate, then up) or null
+    const uint16_t* w2_bias;     // bf16 [E, H] or null (added at the combine)
+    float swiglu_limit;          // > 0: gate and up clamped to [-limit, limit]
     int T, H, I, E, topk, bm;
     int64_t cap;
     int fmt;
+};
+
+// GEMM1 epilogue of one (row, column i): gate g and up u after the expert's
+// optional w13 bias and the optional clamp, as SwiGLU's inputs.
+struct GluTerms {
+    float bg, bu, lim;
+    bool bias;
+    __device__ __forceinline__ void load(const MoeGemmArgs& a, int e, int i) {
+        bias = a.w13_bias != nullptr;
+        lim = a.swiglu_limit;
+        bg = bu = 0.0f;
+        if (bias) {
+            const uint16_t* b = a.w13_bias + (int64_t)e * 2 * a.I;
+            bg = __uint_as_float((uint32_t)b[i] << 16);
+            bu = __uint_as_float((uint32_t)b[a.I + i] << 16);
+        }
+    }
+    __device__ __forceinline__ void apply(float& g, float& u) const {
+        if (bias) {
+            g += bg;
+            u += bu;
+        }
+        if (lim > 0.0f) {
+            g = fminf(fmaxf(g, -lim), lim);
+            u = fminf(fmaxf(u, -lim), lim);
+        }
+    }
 };
 
 // Split-K workgroup kernels (any block size up to 64).
@@ -61,8 +91,11 @@ bool prefill_eligible(const MoeGemmArgs& a);
 int64_t prefill_list_bytes(int64_t cap);
 hipError_t launch_prefill(const MoeGemmArgs& a, int stage, void* list_ws, hipStream_t s);
 
-hipError_t launch_combine(const float* y, const int32_t* ids, const float* weights, int T, int H,
-                          int E, int topk, uint16_t* out, hipStream_t s);
+// out[t] = sum_j weight[t, j] * (y[t*topk + j] + w2_bias[ids[t, j]]) (no
+// bias term when w2_bias is null).
+hipError_t launch_combine(const float* y, const int32_t* ids, const float* weights,
+                          const uint16_t* w2_bias, int T, int H, int E, int topk, uint16_t* out,
+                          hipStream_t s);
 
 hipError_t launch_requant(const uint8_t* w, const uint8_t* scale, int N, int K, int lo, int hi,
                           uint8_t* q, uint16_t* qs, hipStream_t s);

@@ -109,7 +109,9 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 //            loads its MFMA activation operands straight from global memory
 //            (L2) into a ring of registers, so there is no shared tile and
 //            no workgroup barrier; the wave streams its weights on its own.
-template <int STAGE, int FMT, int NB, bool DIRECT, class SH>
+// EPI: compile the optional expert-bias / clamp epilogue of stage 1 (kernels
+// launched without bias or clamp are built without it).
+template <int STAGE, int FMT, int NB, bool DIRECT, class SH, bool EPI = true>
 __device__ __forceinline__ void pf_tile(const MoeGemmArgs& a, SH& sh, int e, int row0, int n0) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -517,6 +519,25 @@ __device__ __forceinline__ void pf_tile(const MoeGemmArgs& a, SH& sh, int e, int
         // results for them are dropped, so their h values are never used.
         const rsrc_t rh = make_rsrc(a.h, (uint32_t)(a.cap * a.I * 2));
         const uint32_t vbase = ((uint32_t)(row0 + 4 * half) * (uint32_t)a.I + (uint32_t)(n0 + 32 * w + nl)) * 2u;
+        // Expert bias / clamp (optional): a separate store loop, so the plain
+        // epilogue is unchanged.
+        if (EPI && (a.w13_bias || a.swiglu_limit > 0.0f)) {
+            GluTerms glu;
+            glu.load(a, e, n0 + 32 * w + nl);
+#pragma unroll
+            for (int i = 0; i < NB; ++i)
+#pragma unroll
+                for (int q = 0; q < 16; ++q) {
+                    const int r = 32 * i + 8 * (q >> 2) + 4 * half + (q & 3);
+                    const int p = sh.rows[r];
+                    const uint32_t soff = (uint32_t)(32 * i + 8 * (q >> 2) + (q & 3)) * (uint32_t)(2 * a.I);
+                    float g = acc[i][0][q], u = acc[i][1][q];
+                    glu.apply(g, u);
+                    __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16_bits(swiglu_fast(g, u)), rh,
+                                                          (p >= 0 && p < P) ? vbase : kOob, soff, 0);
+                }
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < NB; ++i)
 #pragma unroll

@@ -393,6 +393,85 @@ def test_forward_other_block_kernels(moe, T, H, I, E, topk, bm, fmt):
     check_close_bf16_out(out_f64(out), ref, f"other-kernels T={T} H={H} I={I} E={E} k={topk} bm={bm} fmt={fmt}")
 
 
+# Expert biases and the GEMM1 clamp (optional terms of the layer: w13_bias
+# [E, 2I], w2_bias [E, H], swiglu_limit), on every kernel family.
+BIAS_CASES = [
+    # T, H, I, E, topk, bm, fmt, which (b = both biases, c = clamp)
+    (4, 256, 128, 8, 2, None, 0, "bc"),    # GEMV kernels (tiny shape)
+    (4, 256, 128, 8, 2, None, 0, "b"),     # biases only
+    (4, 256, 128, 8, 2, None, 0, "c"),     # clamp only
+    (6, 512, 1024, 16, 4, None, 0, "bc"),  # GEMV, rows reloaded in sequence
+    (2, 512, 1024, 40, 20, None, 0, "bc"), # topk above 16: the combine's slot loop
+    (16, 512, 256, 8, 4, 32, 0, "bc"),     # single-wave MFMA tiles (gate_up and down)
+    (24, 512, 256, 12, 3, 32, 1, "bc"),    # int4 single-wave tiles
+    (256, 512, 512, 8, 4, None, 0, "bc"),  # 4-wave LDS tiles with super-blocks
+    (96, 512, 256, 8, 4, None, 1, "bc"),   # int4 on the 4-wave tiles
+    (20, 288, 160, 6, 3, 32, 0, "bc"),     # wave-per-tile kernels
+    (40, 512, 256, 8, 4, 64, 1, "bc"),     # 64-row workgroup kernels, int4
+]
+
+
+@pytest.mark.parametrize("T,H,I,E,topk,bm,fmt,which", BIAS_CASES)
+def test_forward_bias_clamp(moe, T, H, I, E, topk, bm, fmt, which):
+    wl = synth.small(T=T, H=H, I=I, E=E, topk=topk, seed=13 * T + H + fmt)
+    b13, b2 = synth.biases(E, H, I, seed=T + E)
+    use_b = "b" in which
+    limit = 100.0 if "c" in which else 0.0
+    ids, w = oracle.route_topk(wl.logits, topk)
+    if fmt == 0:
+        wts = weights_dev(wl)
+        r13, rs13, r2, rs2 = wl.w13, wl.w13_scale, wl.w2, wl.w2_scale
+    else:
+        q13, s13 = moe.requantize_mxfp4_experts(dev(wl.w13), dev(wl.w13_scale))
+        q2, s2 = moe.requantize_mxfp4_experts(dev(wl.w2), dev(wl.w2_scale))
+        wts = (q13, s13, q2, s2)
+        r13, rs13 = oracle.requant_int4g32(wl.w13, wl.w13_scale)
+        r2, rs2 = oracle.requant_int4g32(wl.w2, wl.w2_scale)
+    out = moe.moe_a16w4_layer(x_dev(wl), dev(wl.logits), *wts, topk, fmt=fmt, block_m=bm,
+                              w13_bias=dev(b13, torch.bfloat16) if use_b else None,
+                              w2_bias=dev(b2, torch.bfloat16) if use_b else None, swiglu_limit=limit)
+    torch.cuda.synchronize()
+    ref = oracle.moe_forward(wl.x, r13, rs13, r2, rs2, fmt, ids, w, I=I,
+                             w13_bias=b13 if use_b else None, w2_bias=b2 if use_b else None,
+                             swiglu_limit=limit)
+    plain = oracle.moe_forward(wl.x, r13, rs13, r2, rs2, fmt, ids, w, I=I)
+    rms = float(np.sqrt(np.mean(ref ** 2)))
+    assert np.abs(ref - plain).max() > 0.1 * rms  # the terms matter at this scale
+    check_close_bf16_out(out_f64(out), ref, f"bias/clamp {which} T={T} H={H} I={I} E={E} k={topk} bm={bm} fmt={fmt}")
+
+
+@pytest.mark.parametrize("name", ["decode_t1", "decode_t16", "prefill_t1024"])
+def test_forward_bias_clamp_full_size(moe, full_weights, name):
+    """Biases and clamp at the production shape, in the benchmark's launch
+    configuration (GEMV kernels at 1 token, single-wave and 4-wave tiles at
+    16, the prefill tiles at 1024); sampled tokens against the oracle."""
+    wl, w = full_weights(name)
+    s = wl.spec
+    b13, b2 = synth.biases(s.E, s.H, s.I, seed=s.seed + 50)
+    out = moe.moe_a16w4_layer(x_dev(wl), dev(wl.logits), *w, s.topk, w13_bias=dev(b13, torch.bfloat16),
+                              w2_bias=dev(b2, torch.bfloat16), swiglu_limit=100.0)
+    torch.cuda.synchronize()
+    ids, rw = oracle.route_topk(wl.logits, s.topk)
+    tok = _sample_tokens(s.T, 8 if s.T > 16 else 4, seed=s.seed + 1)
+    ref = oracle.moe_forward(wl.x, wl.w13, wl.w13_scale, wl.w2, wl.w2_scale, 0, ids, rw, I=s.I, tokens=tok,
+                             w13_bias=b13, w2_bias=b2, swiglu_limit=100.0)
+    check_close(out_f64(out)[tok], ref, f"bias/clamp {name} tokens {tok.size}/{s.T}")
+
+
+def test_forward_bias_validation(moe):
+    wl = synth.make(synth.specs()["tiny"])
+    s = wl.spec
+    b13, b2 = synth.biases(s.E, s.H, s.I, seed=1)
+    with pytest.raises(moe.MoeError, match="swiglu_limit"):
+        moe.moe_a16w4_layer(x_dev(wl), dev(wl.logits), *weights_dev(wl), s.topk, swiglu_limit=-1.0)
+    with pytest.raises(ValueError, match="w13_bias"):
+        moe.moe_a16w4_layer(x_dev(wl), dev(wl.logits), *weights_dev(wl), s.topk,
+                            w13_bias=dev(b13[:, :-32].copy(), torch.bfloat16))
+    with pytest.raises(ValueError, match="w2_bias"):
+        moe.moe_a16w4_layer(x_dev(wl), dev(wl.logits), *weights_dev(wl), s.topk,
+                            w2_bias=dev(b2[:-1].copy(), torch.bfloat16))
+
+
 def test_layer_on_side_stream_matches_default_stream(moe):
     """stream= on a side stream: the call's own temporaries are allocated on
     that stream; the output equals the default-stream result bit for bit,
