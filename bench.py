@@ -17,8 +17,11 @@ dominant kernel (the gate_up stage): algorithmic bytes (decode) or flops
 on the launch stream around a graph of back-to-back launches cycling over the
 weight sets; its `traffic` is the HBM bytes per launch that rocprofv3 counters
 measured for the same kernel sources (profiles/traffic.json), else null.
-`stage_us` is an eager per-stage breakdown (events between launches, so it
-includes launch gaps). For the int4 workloads `requant` is the load-time
+`stage_us` is an eager breakdown into the monolithic call's two stage groups
+(routing + align/sort + gate_up; down + combine), with events between the
+launches, so it includes launch gaps. `warm` repeats one weight set every
+step (the cold headline rotates over --sets). Prefill lines also carry the
+shader clock sampled under the MFMA load and the peak at that clock. For the int4 workloads `requant` is the load-time
 MXFP4 -> int4-g32 conversion of one weight set (every expert of w13 and w2, 8
 experts per call into preallocated outputs): bytes read + written per pass
 over its duration, against HBM peak. `cpu_baseline` is the CPU oracle on a
@@ -104,16 +107,10 @@ class Layer:
             torch.cuda.synchronize()
         self.w13, self.w13s, self.w2, self.w2s = w
         self.bm = moe.moe_default_block_m(T, k, E)
-        cap = moe.moe_align_sort_capacity(T, k, E, self.bm)
-        self.ids = torch.empty((T, k), dtype=torch.int32, device=dev)
-        self.wts = torch.empty((T, k), dtype=torch.float32, device=dev)
-        self.sort = (torch.empty(cap, dtype=torch.int32, device=dev),
-                     torch.empty(cap // self.bm, dtype=torch.int32, device=dev),
-                     torch.empty(E + 1, dtype=torch.int32, device=dev),
-                     torch.empty(1, dtype=torch.int32, device=dev))
-        self.out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
-        self.ws = torch.empty(moe.moe_a16w4_workspace_size(T, H, I, E, k, self.bm), dtype=torch.uint8,
-                              device=dev)
+        self.bufs = moe.MonolithicBuffers(T, H, I, E, k, self.bm, dev)
+        b = self.bufs
+        self.ids, self.wts, self.out, self.ws = b.ids, b.weights, b.out, b.workspace
+        self.sort = (b.sorted_ids, b.block_expert, b.expert_offsets, b.num_post_pad)
 
     def route_sort(self):
         self.moe.moe_route_align(self.logits, self.k, self.E, self.bm, True, self.ids, self.wts,
@@ -125,29 +122,40 @@ class Layer:
                                    s, be, npp, self.bm, fmt=self.fmt, out=self.out, workspace=self.ws,
                                    stages=stages)
 
+    def monolithic(self, stages=7):
+        self.moe.moe_a16w4_forward_monolithic(self.x, self.logits, self.w13, self.w13s, self.w2, self.w2s,
+                                              self.k, fmt=self.fmt, block_m=self.bm, bufs=self.bufs,
+                                              stages=stages)
+
     def step(self):
-        self.route_sort()
-        self.forward()
+        """One pass of the layer: routing, align/sort, gate_up + SwiGLU, down,
+        combine (moe_a16w4_forward_monolithic)."""
+        self.monolithic()
 
     def distinct_experts(self):
         import torch
         return int(torch.unique(self.ids).numel())
 
 
-def stage1_launch_us(layers, moe, eager, reps=4):
+def stage1_launch_us(layers, moe, eager, fused_t1, reps=4):
     """Average duration of one gate_up launch: a HIP graph of launches cycling
     over every weight set (eager launches with --eager), timed with events on
-    the stream the launches go to."""
+    the stream the launches go to. With the one-token path the launch is the
+    gate_up kernel that also routes (the monolithic call's first stage)."""
     import torch
     stream = torch.cuda.current_stream()
     n = len(layers) * reps
+    if fused_t1:
+        launch = lambda L: L.monolithic(moe.MOE_STAGE_GATE_UP)
+    else:
+        launch = lambda L: L.forward(moe.MOE_STAGE_GATE_UP)
     if eager:
-        fn = lambda: [layers[i % len(layers)].forward(moe.MOE_STAGE_GATE_UP) for i in range(n)]
+        fn = lambda: [launch(layers[i % len(layers)]) for i in range(n)]
     else:
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             for i in range(n):
-                layers[i % len(layers)].forward(moe.MOE_STAGE_GATE_UP)
+                launch(layers[i % len(layers)])
         stream = torch.cuda.current_stream()
         fn = g.replay
     fn()
@@ -183,9 +191,18 @@ def measured_traffic(workload, kernel):
     return rec["hbm_bytes_per_launch"]
 
 
+def fused_t1(T, fmt, H, I, topk, E):
+    """Whether the monolithic call takes the two-launch one-token path (the
+    rule of t1_eligible in the C sources, restated for the label)."""
+    return (T == 1 and fmt == 0 and E <= 128 and topk <= 64 and H % 256 == 0 and I % 128 == 0
+            and H <= 4096 and I <= 4096)
+
+
 def stage1_kernel_name(T, bm, fmt, H, I, topk, E):
     """Which gate_up kernel the library launches for this shape (the rule of
     gemv_eligible / forward_stages in the C sources, restated for the label)."""
+    if fused_t1(T, fmt, H, I, topk, E):
+        return "route_gate_up_t1_kernel"
     rows = min(T, bm)
     if (bm <= 32 and fmt == 0 and rows <= 8 and H <= 4096 and I <= 4096
             and H % 256 == 0 and I % 128 == 0):
@@ -241,26 +258,79 @@ def requant_rate(moe, mx, passes=5):
 
 
 def cpu_baseline(wl, spec, seconds, fmt_name):
-    """The CPU oracle (test infrastructure) timed on this host, tokens/s."""
+    """The CPU oracle (test infrastructure) timed on this host, tokens/s: the
+    same bounded sample (routing + align/sort of every token, the forward of
+    up to 4 of them) on all host cores and on one core, each the median of 3
+    timed runs; a run repeats the sample to about seconds / 6."""
     import numpy as np
     import oracle
     T = wl.x.shape[0]
     n_tok = T if T <= 4 else 2
     tokens = np.arange(n_tok, dtype=np.int32)
-    reps, t0 = 0, time.perf_counter()
-    while True:
+
+    def sample():
         ids, w = oracle.route_topk(wl.logits, spec.topk)
         oracle.align_sort(ids, spec.E, 16)
         oracle.moe_forward(wl.x, wl.w13, wl.w13_scale, wl.w2, wl.w2_scale, oracle.FMT_MXFP4, ids, w,
                            I=spec.I, tokens=tokens if n_tok < T else None)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    return {"value": round(reps * n_tok / el, 4), "unit": "tokens/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
-            "sample": f"{reps} x (route + align/sort of all {T} tokens + forward of {n_tok} token(s)) of "
-                      f"the {fmt_name} workload, weight set 0, {el:.1f} s"}
+
+    def median_rate(threads):
+        oracle.set_num_threads(threads)
+        t0 = time.perf_counter()
+        sample()  # also sizes the runs
+        one = time.perf_counter() - t0
+        reps = max(1, int(seconds / 6 / max(one, 1e-6)))
+        rates = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            for _ in range(reps):
+                sample()
+            rates.append(reps * n_tok / (time.perf_counter() - t0))
+        return float(np.median(rates)), reps
+
+    all_cores = oracle.num_threads()
+    v_all, reps_all = median_rate(all_cores)
+    v_one, reps_one = median_rate(1)
+    oracle.set_num_threads(all_cores)
+    return {"value": round(v_all, 4), "unit": "tokens/s", "cores": all_cores, "kind": "oracle",
+            "one_core": {"value": round(v_one, 4), "cores": 1},
+            "sample": f"median of 3 runs of {reps_all} (all cores) / {reps_one} (one core) x (route + "
+                      f"align/sort of all {T} tokens + forward of {n_tok} token(s)) of the {fmt_name} "
+                      f"workload, weight set 0"}
+
+
+def sampled_sclk_mhz(run_for_s, work):
+    """Shader clock while `work` keeps the GPU busy: rocm-smi's current sclk,
+    sampled by a child process every ~0.2 s over run_for_s seconds of
+    back-to-back work. None when rocm-smi gives no reading."""
+    import re
+    import subprocess
+    import threading
+
+    import torch
+    samples, stop = [], threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            try:
+                r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=5)
+                m = re.search(r"sclk.*?\((\d+)\s*Mhz\)", r.stdout, flags=re.I)
+                if m:
+                    samples.append(int(m.group(1)))
+            except Exception:
+                return
+            stop.wait(0.2)
+
+    th = threading.Thread(target=sampler, daemon=True)
+    th.start()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < run_for_s:
+        for _ in range(20):
+            work()
+        torch.cuda.synchronize()
+    stop.set()
+    th.join(timeout=10)
+    return sorted(samples)[len(samples) // 2] if samples else None
 
 
 def main():
@@ -333,25 +403,37 @@ def main():
     torch.cuda.synchronize()
     ms_per_step = start.elapsed_time(end) / args.steps
 
-    # ---- per-stage timing (eager, events on the launch stream)
+    # ---- warm cache: one weight set replayed every step (its weights partly
+    # served by the Infinity Cache), reported apart from the headline
+    warm_ms = None
+    if graphs is not None:
+        for _ in range(args.warmup):
+            graphs[0].replay()
+        torch.cuda.synchronize()
+        w0, w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        w0.record()
+        for _ in range(args.steps):
+            graphs[0].replay()
+        w1.record()
+        torch.cuda.synchronize()
+        warm_ms = w0.elapsed_time(w1) / args.steps
+
+    # ---- per-stage timing (eager, events on the launch stream): the two
+    # stage groups of the monolithic call
     nst = max(args.steps, 8)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(nst)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(nst)]
     for i in range(min(args.warmup, 4)):
         layers[i % R].step()
     torch.cuda.synchronize()
     for i in range(nst):
         L, e = layers[i % R], ev[i]
         e[0].record()
-        L.route_sort()
+        L.monolithic(moe.MOE_STAGE_GATE_UP)
         e[1].record()
-        L.forward(moe.MOE_STAGE_GATE_UP)
+        L.monolithic(moe.MOE_STAGE_DOWN | moe.MOE_STAGE_COMBINE)
         e[2].record()
-        L.forward(moe.MOE_STAGE_DOWN)
-        e[3].record()
-        L.forward(moe.MOE_STAGE_COMBINE)
-        e[4].record()
     torch.cuda.synchronize()
-    stage_ms = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(4)] for e in ev])
+    stage_ms = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(2)] for e in ev])
     stage_avg = stage_ms.mean(axis=0)
     eager_ms = float(stage_ms.sum(axis=1).mean())
 
@@ -360,6 +442,8 @@ def main():
     w13_b, w2_b = weight_bytes_per_expert(H, I, fmt)
     d_avg = float(np.mean(distinct))
     act_bytes_1 = T * H * 2 + P * I * 2            # x read, h written
+    if fused_t1(T, fmt, H, I, k, E):
+        act_bytes_1 += T * E * 4                    # the routing reads the logits
     stage1_bytes = d_avg * w13_b + act_bytes_1
     layer_bytes = d_avg * (w13_b + w2_b) + 2 * T * H * 2 + T * E * 4
     stage1_flops = 2.0 * P * (2 * I) * H
@@ -367,12 +451,23 @@ def main():
 
     # ---- dominant kernel (gate_up): back-to-back launches over all sets,
     # HIP events on the launch stream, average duration per launch
-    s1_us = stage1_launch_us(layers, moe, args.eager)
+    t1 = fused_t1(T, fmt, H, I, k, E)
+    s1_us = stage1_launch_us(layers, moe, args.eager, t1)
     s1_sec = s1_us * 1e-6
     if spec.T >= 256:
         ach = stage1_flops / s1_sec / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(ach / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": None}
+        # The published peak is quoted at 2.4 GHz; the clock the chip holds
+        # under this MFMA load (rocm-smi's sclk while the step replays) gives
+        # the peak the kernel can reach here.
+        work = graphs[0].replay if graphs is not None else layers[0].step
+        mhz = sampled_sclk_mhz(1.5, work)
+        if mhz:
+            at_clock = BF16_MFMA_PEAK_TFLOPS * mhz / 2400.0
+            roof["sclk_mhz_observed"] = mhz
+            roof["peak_at_observed_clock"] = round(at_clock, 1)
+            roof["frac_at_observed_clock"] = round(ach / at_clock, 4)
     else:
         ach = stage1_bytes / s1_sec / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
@@ -405,10 +500,13 @@ def main():
         "layer_hbm_gbps": round(layer_bytes / (ms_per_step * 1e-3) / 1e9, 1),
         "layer_tflops": round(layer_flops / (ms_per_step * 1e-3) / 1e12, 2),
         "eager_ms_per_step": round(eager_ms, 5),
-        "stage_us": {"route_sort": round(stage_avg[0] * 1e3, 2), "gate_up": round(stage_avg[1] * 1e3, 2),
-                     "down": round(stage_avg[2] * 1e3, 2), "combine": round(stage_avg[3] * 1e3, 2)},
+        "stage_us": {"route_sort_gate_up": round(stage_avg[0] * 1e3, 2),
+                     "down_combine": round(stage_avg[1] * 1e3, 2)},
         "roofline": roof,
     }
+    if warm_ms is not None:
+        line["warm"] = {"ms_per_step": round(warm_ms, 5), "value": round(T / (warm_ms * 1e-3), 2),
+                        "unit": "tokens/s", "note": "one weight set replayed every step (Infinity Cache warm)"}
     if int4:
         line["requant"] = requant_rate(moe, layers[0].mx)
     if not args.no_cpu_baseline:

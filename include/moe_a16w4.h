@@ -205,6 +205,33 @@ moe_status moe_a16w4_forward_ex(const uint16_t* x, const uint8_t* w13, const voi
                                 void* workspace, size_t workspace_bytes, unsigned stages,
                                 void* stream);
 
+/* The whole layer from router logits (apply_monolithic on the mxfp4 API
+ * page: routing inside the kernels): moe_route_align for
+ * (router_logits, renormalize, block_m) into topk_ids, topk_weights,
+ * sorted_ids, block_expert, expert_offsets and num_post_pad (all outputs,
+ * sized as for moe_route_align), then moe_a16w4_forward_ex. Results equal
+ * those two calls (routing and align/sort outputs bit for bit, out bit for
+ * bit as well), with fewer launches where the shape allows: one token with
+ * MXFP4 weights, E <= 128, H a multiple of 256 and I of 128 (both up to
+ * 4096) routes inside the gate_up kernel (no separate routing launch).
+ *   router_logits  fp32 [T, E] (16-byte aligned).
+ *   stages         MOE_STAGE_ALL, MOE_STAGE_GATE_UP (routing, align/sort and
+ *                  gate_up) or MOE_STAGE_DOWN | MOE_STAGE_COMBINE (the rest);
+ *                  other masks give MOE_ERR_INVALID_ARG.
+ * Requirements and limits: those of moe_route_align and moe_a16w4_forward_ex;
+ * the workspace is moe_a16w4_workspace_size bytes. */
+moe_status moe_a16w4_forward_monolithic(const uint16_t* x, const float* router_logits,
+                                        const uint8_t* w13, const void* w13_scale,
+                                        const uint16_t* w13_bias, const uint8_t* w2,
+                                        const void* w2_scale, const uint16_t* w2_bias,
+                                        moe_wfmt fmt, moe_act act, float swiglu_limit,
+                                        int renormalize, int T, int H, int I, int E, int topk,
+                                        int block_m, int32_t* topk_ids, float* topk_weights,
+                                        int32_t* sorted_ids, int32_t* block_expert,
+                                        int32_t* expert_offsets, int32_t* num_post_pad,
+                                        uint16_t* out, void* workspace, size_t workspace_bytes,
+                                        unsigned stages, void* stream);
+
 /* moe_a16w4_forward without a workspace argument, for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving
  * loops, harnesses that forbid hipMalloc). The workspace is the library's

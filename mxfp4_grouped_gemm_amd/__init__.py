@@ -10,7 +10,8 @@ library has not been built.
 Functions mirror the C ABI names:
   moe_route_topk, moe_align_sort_capacity, moe_default_block_m,
   moe_align_sort, moe_route_align, moe_a16w4_workspace_size, moe_a16w4_forward,
-  moe_a16w4_forward_stages, moe_a16w4_forward_ex, moe_a16w4_forward_noalloc,
+  moe_a16w4_forward_stages, moe_a16w4_forward_ex, moe_a16w4_forward_monolithic,
+  moe_a16w4_forward_noalloc,
   mxfp4_to_int4g32_requant, moe_last_error
 plus two compositions: moe_a16w4_layer (route -> sort -> forward, the
 in-kernel routing path of apply_monolithic on the vLLM mxfp4 API page) and
@@ -36,7 +37,8 @@ MOE_STAGE_GATE_UP, MOE_STAGE_DOWN, MOE_STAGE_COMBINE, MOE_STAGE_ALL = 1, 2, 4, 7
 EXPORTS = (
     "moe_last_error", "moe_route_topk", "moe_align_sort_capacity", "moe_default_block_m",
     "moe_align_sort", "moe_route_align", "moe_a16w4_workspace_size", "moe_a16w4_forward",
-    "moe_a16w4_forward_stages", "moe_a16w4_forward_ex", "moe_a16w4_forward_noalloc",
+    "moe_a16w4_forward_stages", "moe_a16w4_forward_ex", "moe_a16w4_forward_monolithic",
+    "moe_a16w4_forward_noalloc",
     "mxfp4_to_int4g32_requant",
 )
 # Scratch of the allocation-free forward (MOE_NOALLOC_SCRATCH_BYTES).
@@ -78,6 +80,9 @@ def _load():
     L.moe_a16w4_forward_ex.restype = i
     L.moe_a16w4_forward_ex.argtypes = [p, p, p, p, p, p, p, i, i, ctypes.c_float, p, p, p, p, p, i, i, i, i,
                                        i, i, p, p, sz, ctypes.c_uint, p]
+    L.moe_a16w4_forward_monolithic.restype = i
+    L.moe_a16w4_forward_monolithic.argtypes = [p, p, p, p, p, p, p, p, i, i, ctypes.c_float, i, i, i, i, i,
+                                               i, i, p, p, p, p, p, p, p, p, sz, ctypes.c_uint, p]
     L.moe_a16w4_forward_noalloc.restype = i
     L.moe_a16w4_forward_noalloc.argtypes = [p, p, p, p, p, i, i, p, p, p, p, p, i, i, i, i, i, i, p, p]
     L.mxfp4_to_int4g32_requant.restype = i
@@ -305,22 +310,72 @@ def moe_a16w4_forward_noalloc(x, w13, w13_scale, w2, w2_scale, topk_ids, topk_we
     return out
 
 
+class MonolithicBuffers:
+    """Every device buffer of moe_a16w4_forward_monolithic for one shape:
+    the routing and align/sort outputs, the workspace and the output."""
+
+    def __init__(self, T, H, I, E, topk, block_m, device, stream=None):
+        cap = moe_align_sort_capacity(T, topk, E, block_m)
+        need = moe_a16w4_workspace_size(T, H, I, E, topk, block_m)
+        if cap < 0 or need < 0:
+            raise MoeError(MOE_ERR_INVALID_ARG, f"invalid sizes T={T} H={H} I={I} E={E} topk={topk} "
+                           f"block_m={block_m}")
+        self.block_m = block_m
+        with _on(stream):
+            self.ids = torch.empty((T, topk), dtype=torch.int32, device=device)
+            self.weights = torch.empty((T, topk), dtype=torch.float32, device=device)
+            self.sorted_ids = torch.empty(max(cap, 1), dtype=torch.int32, device=device)
+            self.block_expert = torch.empty(max(cap // block_m, 1), dtype=torch.int32, device=device)
+            self.expert_offsets = torch.empty(E + 1, dtype=torch.int32, device=device)
+            self.num_post_pad = torch.empty(1, dtype=torch.int32, device=device)
+            self.workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+            self.out = torch.empty((T, H), dtype=torch.bfloat16, device=device)
+
+
+def moe_a16w4_forward_monolithic(x, router_logits, w13, w13_scale, w2, w2_scale, topk, fmt=MOE_W_MXFP4,
+                                 act=MOE_ACT_SWIGLU, renormalize=True, block_m=None, bufs=None,
+                                 w13_bias=None, w2_bias=None, swiglu_limit=0.0, stages=MOE_STAGE_ALL,
+                                 stream=None):
+    """The layer from router logits in one call (apply_monolithic): routing,
+    align/sort and the forward. `bufs` (MonolithicBuffers) holds every
+    device buffer; one is allocated on `stream` when not given. Returns
+    bufs (bufs.out is the layer output; bufs.ids / bufs.weights the routing)."""
+    _dev(x, "x", torch.bfloat16, 2)
+    _dev(router_logits, "router_logits", torch.float32, 2)
+    E, H, I = _weights(w13, w13_scale, w2, w2_scale, fmt)
+    T = x.shape[0]
+    if x.shape[1] != H or tuple(router_logits.shape) != (T, E):
+        raise ValueError(f"x {tuple(x.shape)} / router_logits {tuple(router_logits.shape)} do not match "
+                         f"H={H}, E={E}")
+    bm = moe_default_block_m(T, topk, E) if block_m is None else int(block_m)
+    if bufs is None:
+        bufs = MonolithicBuffers(T, H, I, E, topk, bm, x.device, stream)
+    elif bufs.block_m != bm:
+        raise ValueError(f"buffers were sized for block_m={bufs.block_m}, not {bm}")
+    _bias(w13_bias, "w13_bias", (E, 2 * I))
+    _bias(w2_bias, "w2_bias", (E, H))
+    b = bufs
+    _check(lib.moe_a16w4_forward_monolithic(
+        _ptr(x), _ptr(router_logits), _ptr(w13), _ptr(w13_scale), _ptr(w13_bias), _ptr(w2), _ptr(w2_scale),
+        _ptr(w2_bias), int(fmt), int(act), float(swiglu_limit), int(bool(renormalize)), T, H, I, E, int(topk),
+        bm, _ptr(b.ids), _ptr(b.weights), _ptr(b.sorted_ids), _ptr(b.block_expert), _ptr(b.expert_offsets),
+        _ptr(b.num_post_pad), _ptr(b.out), _ptr(b.workspace), b.workspace.numel(), int(stages),
+        _stream(stream)))
+    return bufs
+
+
 def moe_a16w4_layer(x, router_logits, w13, w13_scale, w2, w2_scale, topk, fmt=MOE_W_MXFP4,
                     renormalize=True, block_m=None, stream=None, w13_bias=None, w2_bias=None,
                     swiglu_limit=0.0):
-    """route -> align/sort -> forward on one stream (no host synchronisation).
-    With an explicit `stream` every tensor the call creates is allocated on
-    that stream (the routing and sort arrays, the workspace and the output),
-    so their memory stays reserved until the stream's work is done; the
-    caller orders any use of the output on another stream as usual."""
-    E = w13.shape[0]
-    T = x.shape[0]
-    bm = moe_default_block_m(T, topk, E) if block_m is None else block_m
-    ids, w, sorted_ids, block_expert, _, npp = moe_route_align(router_logits, topk, E, bm, renormalize,
-                                                              stream=stream)
-    return moe_a16w4_forward(x, w13, w13_scale, w2, w2_scale, ids, w, sorted_ids, block_expert, npp,
-                             bm, fmt=fmt, stream=stream, w13_bias=w13_bias, w2_bias=w2_bias,
-                             swiglu_limit=swiglu_limit)
+    """route -> align/sort -> forward on one stream (no host synchronisation),
+    through moe_a16w4_forward_monolithic. With an explicit `stream` every
+    tensor the call creates is allocated on that stream (the routing and
+    sort arrays, the workspace and the output), so their memory stays
+    reserved until the stream's work is done; the caller orders any use of
+    the output on another stream as usual."""
+    return moe_a16w4_forward_monolithic(x, router_logits, w13, w13_scale, w2, w2_scale, topk, fmt=fmt,
+                                        renormalize=renormalize, block_m=block_m, w13_bias=w13_bias,
+                                        w2_bias=w2_bias, swiglu_limit=swiglu_limit, stream=stream).out
 
 
 def mxfp4_to_int4g32_requant(w, scale_e8m0, expert_lo, expert_hi, w_int4, scale_bf16, stream=None):

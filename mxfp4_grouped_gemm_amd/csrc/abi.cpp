@@ -69,6 +69,143 @@ WsLayout ws_layout(int T, int H, int I, int E, int topk, int bm) {
     return L;
 }
 
+// Every check of the forward, before anything is enqueued; fills the
+// kernel arguments and the workspace layout. A call with T == 0 passes with
+// a.T == 0 (nothing to launch).
+moe_status prepare_forward(const char* fn, const uint16_t* x, const uint8_t* w13, const void* w13_scale,
+                           const uint16_t* w13_bias, const uint8_t* w2, const void* w2_scale,
+                           const uint16_t* w2_bias, moe_wfmt fmt, moe_act act, float swiglu_limit,
+                           const int32_t* topk_ids, const float* topk_weights,
+                           const int32_t* sorted_ids, const int32_t* block_expert,
+                           const int32_t* num_post_pad, int T, int H, int I, int E, int topk,
+                           int block_m, uint16_t* out, void* workspace, size_t workspace_bytes,
+                           moe::MoeGemmArgs& a, WsLayout& L) {
+    a.T = 0;
+    if (!(swiglu_limit >= 0.0f))
+        return fail(MOE_ERR_INVALID_ARG, "%s: swiglu_limit %g must be >= 0 (0 = no clamp)", fn,
+                    (double)swiglu_limit);
+    if (act != MOE_ACT_SWIGLU)
+        return fail(MOE_ERR_UNSUPPORTED, "%s: activation %d is not implemented (only SwiGLU); "
+                    "refusing to compute a different activation", fn, (int)act);
+    if (fmt != MOE_W_MXFP4 && fmt != MOE_W_INT4G32)
+        return fail(MOE_ERR_UNSUPPORTED, "%s: weight format %d unknown", fn, (int)fmt);
+    if (T < 0) return fail(MOE_ERR_INVALID_ARG, "%s: T=%d < 0", fn, T);
+    if (H < 32 || H % 32 != 0) return fail(MOE_ERR_INVALID_ARG, "%s: H=%d must be a positive multiple of 32", fn, H);
+    if (I < 32 || I % 32 != 0) return fail(MOE_ERR_INVALID_ARG, "%s: I=%d must be a positive multiple of 32", fn, I);
+    if (E < 1) return fail(MOE_ERR_INVALID_ARG, "%s: E=%d < 1", fn, E);
+    if (topk < 1 || topk > E) return fail(MOE_ERR_INVALID_ARG, "%s: topk=%d outside [1, E=%d]", fn, topk, E);
+    if (!valid_bm(block_m)) return fail(MOE_ERR_INVALID_ARG, "%s: block_m=%d invalid", fn, block_m);
+    if (!forward_bm(block_m))
+        return fail(MOE_ERR_UNSUPPORTED, "%s: block_m=%d not implemented (16, 32, 64)", fn, block_m);
+    const int64_t P = (int64_t)T * topk;
+    const int64_t cap = capacity(T, topk, E, block_m);
+    if (P + cap >= (int64_t)0x7fffffff)
+        return fail(MOE_ERR_UNSUPPORTED, "%s: problem too large", fn);
+    // The activation kernels address x [T, H] and h [cap, I] through buffer
+    // records of at most 2^31 bytes (their masked lanes use offsets past
+    // 2^31), and the 64-row kernels index blocks by grid.y.
+    if ((int64_t)T * H * 2 > kMaxRecordBytes || cap * I * 2 > kMaxRecordBytes)
+        return fail(MOE_ERR_UNSUPPORTED,
+                    "%s: T=%d gives activations beyond 2^31 bytes (x %lld B, h %lld B); "
+                    "split the batch", fn, T, (long long)((int64_t)T * H * 2), (long long)(cap * I * 2));
+    if (block_m == 64 && cap / block_m > kMaxGridY)
+        return fail(MOE_ERR_UNSUPPORTED, "%s: %lld blocks of 64 rows exceed the grid", fn,
+                    (long long)(cap / block_m));
+    if (T == 0) return MOE_OK;  // nothing to launch (a.T == 0)
+    const void* ptrs[] = {x, w13, w13_scale, w2, w2_scale, topk_ids, topk_weights,
+                          sorted_ids, block_expert, num_post_pad, out, workspace};
+    for (const void* p : ptrs)
+        if (!p) return fail(MOE_ERR_INVALID_ARG, "%s: null pointer", fn);
+    for (const void* p : ptrs)
+        if (!aligned(p, 16)) return fail(MOE_ERR_INVALID_ARG, "%s: pointer %p not 16-byte aligned", fn, p);
+    if (!aligned(workspace, 256)) return fail(MOE_ERR_INVALID_ARG, "%s: workspace not 256-byte aligned", fn);
+    if (!aligned(w13_bias, 16) || !aligned(w2_bias, 16))
+        return fail(MOE_ERR_INVALID_ARG, "%s: bias pointers must be 16-byte aligned", fn);
+    L = ws_layout(T, H, I, E, topk, block_m);
+    if ((int64_t)workspace_bytes < L.total)
+        return fail(MOE_ERR_INVALID_ARG, "%s: workspace %zu bytes < %lld needed", fn, workspace_bytes,
+                    (long long)L.total);
+
+    a.x = x;
+    a.w13 = w13;
+    a.w13_scale = w13_scale;
+    a.w2 = w2;
+    a.w2_scale = w2_scale;
+    a.sorted_ids = sorted_ids;
+    a.block_expert = block_expert;
+    a.num_post_pad = num_post_pad;
+    a.h = (uint16_t*)((char*)workspace + L.h_off);
+    a.y = (float*)((char*)workspace + L.y_off);
+    a.T = T;
+    a.H = H;
+    a.I = I;
+    a.E = E;
+    a.topk = topk;
+    a.bm = block_m;
+    a.cap = cap;
+    a.fmt = (int)fmt;
+    a.topk_ids = topk_ids;
+    a.topk_weights = topk_weights;
+    a.out = out;
+    a.w13_bias = w13_bias;
+    a.w2_bias = w2_bias;
+    a.swiglu_limit = swiglu_limit;
+    return MOE_OK;
+}
+
+// Routing and align/sort for validated arguments: one launch where the
+// fused kernel applies, else the two kernels.
+moe_status launch_route_align_any(const float* logits, int T, int E, int topk, int renormalize, int block_m,
+                                  int64_t cap, int32_t* topk_ids, float* topk_weights, int32_t* sorted_ids,
+                                  int32_t* block_expert, int32_t* expert_offsets, int32_t* num_post_pad,
+                                  const char* fn, hipStream_t s) {
+    const int64_t P = (int64_t)T * topk;
+    if (T > 0 && moe::route_align_fusable(T, E, topk))
+        return hip_status(moe::launch_route_align(logits, T, E, topk, renormalize, block_m, cap, topk_ids,
+                                                  topk_weights, sorted_ids, block_expert, expert_offsets,
+                                                  num_post_pad, s),
+                          fn);
+    if (T > 0) {
+        const moe_status st = hip_status(
+            moe::launch_route_topk(logits, T, E, topk, renormalize, topk_ids, topk_weights, s), fn);
+        if (st != MOE_OK) return st;
+    }
+    return hip_status(moe::launch_align_sort(topk_ids, (int)P, E, block_m, cap, sorted_ids, block_expert,
+                                             expert_offsets, num_post_pad, s),
+                      fn);
+}
+
+// The forward's launches for prepared arguments (stages: MOE_STAGE_* bits).
+moe_status launch_forward(const moe::MoeGemmArgs& a, const WsLayout& L, void* workspace, unsigned stages,
+                          hipStream_t s) {
+    const int64_t P = (int64_t)a.T * a.topk;
+    const int block_m = a.bm;
+    moe_status st = MOE_OK;
+    // Kernel family per shape: GEMV waves for blocks of <= 8 token rows,
+    // the LDS-tiled MFMA kernels at prefill sizes, wave-per-tile MFMA
+    // kernels for other 16/32-row blocks, split-K workgroups for 64.
+    const bool decode = block_m <= 32;
+    const bool gemv = decode && moe::gemv_eligible(a);
+    const bool prefill = !gemv && moe::prefill_eligible(a) && P >= moe::kPrefillMinPairs;
+    void* list = (char*)workspace + L.list_off;
+    if (stages & MOE_STAGE_GATE_UP) {
+        st = hip_status(prefill ? moe::launch_prefill(a, 1, list, s)
+                        : decode ? moe::launch_decode_stage(a, 1, s) : moe::launch_stage1(a, s),
+                        "moe_a16w4_forward (gate_up)");
+        if (st != MOE_OK) return st;
+    }
+    if (stages & MOE_STAGE_DOWN) {
+        st = hip_status(prefill ? moe::launch_prefill(a, 2, list, s)
+                        : decode ? moe::launch_decode_stage(a, 2, s) : moe::launch_stage2(a, s),
+                        "moe_a16w4_forward (down)");
+        if (st != MOE_OK) return st;
+    }
+    if (stages & MOE_STAGE_COMBINE)
+        st = hip_status(moe::launch_combine(a.y, a.topk_ids, a.topk_weights, a.w2_bias, a.T, a.H, a.E, a.topk, a.out, s),
+                        "moe_a16w4_forward (combine)");
+    return st;
+}
+
 }  // namespace
 
 extern "C" {
@@ -146,21 +283,9 @@ moe_status moe_route_align(const float* logits, int T, int E, int topk, int reno
                           num_post_pad};
     for (const void* p : ptrs)
         if (!aligned(p, 4)) return fail(MOE_ERR_INVALID_ARG, "%s: misaligned pointer", fn);
-    hipStream_t s = (hipStream_t)stream;
-    if (T > 0 && moe::route_align_fusable(T, E, topk))
-        return hip_status(moe::launch_route_align(logits, T, E, topk, renormalize, block_m, cap,
-                                                  topk_ids, topk_weights, sorted_ids, block_expert,
-                                                  expert_offsets, num_post_pad, s),
-                          fn);
-    if (T > 0) {
-        moe_status st = hip_status(moe::launch_route_topk(logits, T, E, topk, renormalize, topk_ids,
-                                                          topk_weights, s),
-                                   fn);
-        if (st != MOE_OK) return st;
-    }
-    return hip_status(moe::launch_align_sort(topk_ids, (int)P, E, block_m, cap, sorted_ids,
-                                             block_expert, expert_offsets, num_post_pad, s),
-                      fn);
+    return launch_route_align_any(logits, T, E, topk, renormalize, block_m, cap, topk_ids, topk_weights,
+                                  sorted_ids, block_expert, expert_offsets, num_post_pad, fn,
+                                  (hipStream_t)stream);
 }
 
 int64_t moe_a16w4_workspace_size(int T, int H, int I, int E, int topk, int block_m) {
@@ -206,101 +331,57 @@ moe_status moe_a16w4_forward_ex(const uint16_t* x, const uint8_t* w13, const voi
     const char* fn = "moe_a16w4_forward";
     if (stages == 0 || (stages & ~MOE_STAGE_ALL))
         return fail(MOE_ERR_INVALID_ARG, "%s: stage mask 0x%x invalid", fn, stages);
-    if (!(swiglu_limit >= 0.0f))
-        return fail(MOE_ERR_INVALID_ARG, "%s: swiglu_limit %g must be >= 0 (0 = no clamp)", fn,
-                    (double)swiglu_limit);
-    if (act != MOE_ACT_SWIGLU)
-        return fail(MOE_ERR_UNSUPPORTED, "%s: activation %d is not implemented (only SwiGLU); "
-                    "refusing to compute a different activation", fn, (int)act);
-    if (fmt != MOE_W_MXFP4 && fmt != MOE_W_INT4G32)
-        return fail(MOE_ERR_UNSUPPORTED, "%s: weight format %d unknown", fn, (int)fmt);
-    if (T < 0) return fail(MOE_ERR_INVALID_ARG, "%s: T=%d < 0", fn, T);
-    if (H < 32 || H % 32 != 0) return fail(MOE_ERR_INVALID_ARG, "%s: H=%d must be a positive multiple of 32", fn, H);
-    if (I < 32 || I % 32 != 0) return fail(MOE_ERR_INVALID_ARG, "%s: I=%d must be a positive multiple of 32", fn, I);
-    if (E < 1) return fail(MOE_ERR_INVALID_ARG, "%s: E=%d < 1", fn, E);
-    if (topk < 1 || topk > E) return fail(MOE_ERR_INVALID_ARG, "%s: topk=%d outside [1, E=%d]", fn, topk, E);
-    if (!valid_bm(block_m)) return fail(MOE_ERR_INVALID_ARG, "%s: block_m=%d invalid", fn, block_m);
-    if (!forward_bm(block_m))
-        return fail(MOE_ERR_UNSUPPORTED, "%s: block_m=%d not implemented (16, 32, 64)", fn, block_m);
-    const int64_t P = (int64_t)T * topk;
-    const int64_t cap = capacity(T, topk, E, block_m);
-    if (P + cap >= (int64_t)0x7fffffff)
-        return fail(MOE_ERR_UNSUPPORTED, "%s: problem too large", fn);
-    // The activation kernels address x [T, H] and h [cap, I] through buffer
-    // records of at most 2^31 bytes (their masked lanes use offsets past
-    // 2^31), and the 64-row kernels index blocks by grid.y.
-    if ((int64_t)T * H * 2 > kMaxRecordBytes || cap * I * 2 > kMaxRecordBytes)
-        return fail(MOE_ERR_UNSUPPORTED,
-                    "%s: T=%d gives activations beyond 2^31 bytes (x %lld B, h %lld B); "
-                    "split the batch", fn, T, (long long)((int64_t)T * H * 2), (long long)(cap * I * 2));
-    if (block_m == 64 && cap / block_m > kMaxGridY)
-        return fail(MOE_ERR_UNSUPPORTED, "%s: %lld blocks of 64 rows exceed the grid", fn,
-                    (long long)(cap / block_m));
-    if (T == 0) return MOE_OK;
-    const void* ptrs[] = {x, w13, w13_scale, w2, w2_scale, topk_ids, topk_weights,
-                          sorted_ids, block_expert, num_post_pad, out, workspace};
-    for (const void* p : ptrs)
-        if (!p) return fail(MOE_ERR_INVALID_ARG, "%s: null pointer", fn);
-    for (const void* p : ptrs)
-        if (!aligned(p, 16)) return fail(MOE_ERR_INVALID_ARG, "%s: pointer %p not 16-byte aligned", fn, p);
-    if (!aligned(workspace, 256)) return fail(MOE_ERR_INVALID_ARG, "%s: workspace not 256-byte aligned", fn);
-    if (!aligned(w13_bias, 16) || !aligned(w2_bias, 16))
-        return fail(MOE_ERR_INVALID_ARG, "%s: bias pointers must be 16-byte aligned", fn);
-    const WsLayout L = ws_layout(T, H, I, E, topk, block_m);
-    if ((int64_t)workspace_bytes < L.total)
-        return fail(MOE_ERR_INVALID_ARG, "%s: workspace %zu bytes < %lld needed", fn, workspace_bytes,
-                    (long long)L.total);
-
     moe::MoeGemmArgs a;
-    a.x = x;
-    a.w13 = w13;
-    a.w13_scale = w13_scale;
-    a.w2 = w2;
-    a.w2_scale = w2_scale;
-    a.sorted_ids = sorted_ids;
-    a.block_expert = block_expert;
-    a.num_post_pad = num_post_pad;
-    a.h = (uint16_t*)((char*)workspace + L.h_off);
-    a.y = (float*)((char*)workspace + L.y_off);
-    a.T = T;
-    a.H = H;
-    a.I = I;
-    a.E = E;
-    a.topk = topk;
-    a.bm = block_m;
-    a.cap = cap;
-    a.fmt = (int)fmt;
-    a.topk_ids = topk_ids;
-    a.topk_weights = topk_weights;
-    a.out = out;
-    a.w13_bias = w13_bias;
-    a.w2_bias = w2_bias;
-    a.swiglu_limit = swiglu_limit;
+    WsLayout L;
+    const moe_status st = prepare_forward(fn, x, w13, w13_scale, w13_bias, w2, w2_scale, w2_bias, fmt, act,
+                                          swiglu_limit, topk_ids, topk_weights, sorted_ids, block_expert,
+                                          num_post_pad, T, H, I, E, topk, block_m, out, workspace,
+                                          workspace_bytes, a, L);
+    if (st != MOE_OK || a.T == 0) return st;
+    return launch_forward(a, L, workspace, stages, (hipStream_t)stream);
+}
+
+moe_status moe_a16w4_forward_monolithic(const uint16_t* x, const float* router_logits, const uint8_t* w13,
+                                        const void* w13_scale, const uint16_t* w13_bias, const uint8_t* w2,
+                                        const void* w2_scale, const uint16_t* w2_bias, moe_wfmt fmt,
+                                        moe_act act, float swiglu_limit, int renormalize, int T, int H,
+                                        int I, int E, int topk, int block_m, int32_t* topk_ids,
+                                        float* topk_weights, int32_t* sorted_ids, int32_t* block_expert,
+                                        int32_t* expert_offsets, int32_t* num_post_pad, uint16_t* out,
+                                        void* workspace, size_t workspace_bytes, unsigned stages,
+                                        void* stream) {
+    const char* fn = "moe_a16w4_forward_monolithic";
+    const unsigned down_combine = MOE_STAGE_DOWN | MOE_STAGE_COMBINE;
+    if (stages != MOE_STAGE_ALL && stages != MOE_STAGE_GATE_UP && stages != down_combine)
+        return fail(MOE_ERR_INVALID_ARG, "%s: stage mask 0x%x invalid (all, gate_up, or down|combine)", fn,
+                    stages);
+    if (E < 1 || E > 1024) return fail(MOE_ERR_UNSUPPORTED, "%s: E=%d outside [1, 1024]", fn, E);
+    if (topk > 64) return fail(MOE_ERR_UNSUPPORTED, "%s: topk=%d > 64", fn, topk);
+    moe::MoeGemmArgs a;
+    WsLayout L;
+    moe_status st = prepare_forward(fn, x, w13, w13_scale, w13_bias, w2, w2_scale, w2_bias, fmt, act,
+                                    swiglu_limit, topk_ids, topk_weights, sorted_ids, block_expert,
+                                    num_post_pad, T, H, I, E, topk, block_m, out, workspace, workspace_bytes,
+                                    a, L);
+    if (st != MOE_OK || a.T == 0) return st;
+    if (!router_logits || !expert_offsets)
+        return fail(MOE_ERR_INVALID_ARG, "%s: null pointer", fn);
+    if (!aligned(router_logits, 16) || !aligned(expert_offsets, 4))
+        return fail(MOE_ERR_INVALID_ARG, "%s: misaligned pointer", fn);
     hipStream_t s = (hipStream_t)stream;
-    moe_status st = MOE_OK;
-    // Kernel family per shape: GEMV waves for blocks of <= 8 token rows,
-    // the LDS-tiled MFMA kernels at prefill sizes, wave-per-tile MFMA
-    // kernels for other 16/32-row blocks, split-K workgroups for 64.
-    const bool decode = block_m <= 32;
-    const bool gemv = decode && moe::gemv_eligible(a);
-    const bool prefill = !gemv && moe::prefill_eligible(a) && P >= moe::kPrefillMinPairs;
-    void* list = (char*)workspace + L.list_off;
+    if (moe::t1_eligible(a))
+        return hip_status(moe::launch_t1_layer(a, router_logits, renormalize, topk_ids, topk_weights, sorted_ids,
+                                               block_expert, expert_offsets, num_post_pad,
+                                               ((stages & MOE_STAGE_GATE_UP) ? 1u : 0u) |
+                                                   ((stages & down_combine) ? 2u : 0u),
+                                               s),
+                          fn);
     if (stages & MOE_STAGE_GATE_UP) {
-        st = hip_status(prefill ? moe::launch_prefill(a, 1, list, s)
-                        : decode ? moe::launch_decode_stage(a, 1, s) : moe::launch_stage1(a, s),
-                        "moe_a16w4_forward (gate_up)");
+        st = launch_route_align_any(router_logits, T, E, topk, renormalize, block_m, a.cap, topk_ids,
+                                    topk_weights, sorted_ids, block_expert, expert_offsets, num_post_pad, fn, s);
         if (st != MOE_OK) return st;
     }
-    if (stages & MOE_STAGE_DOWN) {
-        st = hip_status(prefill ? moe::launch_prefill(a, 2, list, s)
-                        : decode ? moe::launch_decode_stage(a, 2, s) : moe::launch_stage2(a, s),
-                        "moe_a16w4_forward (down)");
-        if (st != MOE_OK) return st;
-    }
-    if (stages & MOE_STAGE_COMBINE)
-        st = hip_status(moe::launch_combine(a.y, topk_ids, topk_weights, w2_bias, T, H, E, topk, out, s),
-                        "moe_a16w4_forward (combine)");
-    return st;
+    return launch_forward(a, L, workspace, stages, s);
 }
 
 moe_status mxfp4_to_int4g32_requant(const uint8_t* w, const uint8_t* scale_e8m0, int E, int N, int K,

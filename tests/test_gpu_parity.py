@@ -472,6 +472,85 @@ def test_forward_bias_validation(moe):
                             w2_bias=dev(b2[:-1].copy(), torch.bfloat16))
 
 
+# The layer from router logits in one call. One token with MXFP4 weights
+# runs as two launches (routing inside gate_up, down with the combine); the
+# routing and align/sort outputs must equal moe_route_align's bit for bit,
+# and the output the oracle's.
+MONO_CASES = [
+    # T, H, I, E, topk, bm, renorm, bias
+    (1, 3584, 3072, 112, 15, 16, True, False),   # the production expert-parallel shape
+    (1, 3584, 3072, 112, 15, 32, True, True),    # with biases and clamp, 32-row blocks
+    (1, 256, 128, 8, 3, 16, True, False),        # smallest H and I of the path
+    (1, 512, 384, 128, 64, 16, True, False),     # 128 experts, 64 slots, I = 384
+    (1, 4096, 4096, 64, 7, 64, False, False),    # largest H and I, no renormalisation
+    (1, 1024, 512, 1, 1, 16, True, True),        # a single expert
+    (1, 512, 256, 200, 8, 16, True, False),      # more than 128 experts: routed separately
+    (3, 512, 256, 16, 4, 16, True, True),        # several tokens: route_align + forward
+]
+
+
+@pytest.mark.parametrize("T,H,I,E,topk,bm,renorm,bias", MONO_CASES)
+def test_forward_monolithic(moe, T, H, I, E, topk, bm, renorm, bias):
+    wl = synth.small(T=T, H=H, I=I, E=E, topk=topk, seed=17 * T + E + H, scale_lo=118, scale_hi=128)
+    w = weights_dev(wl)
+    b13, b2 = synth.biases(E, H, I, seed=E + 1) if bias else (None, None)
+    kw = dict(w13_bias=dev(b13, torch.bfloat16), w2_bias=dev(b2, torch.bfloat16), swiglu_limit=100.0) if bias else {}
+    logits = dev(wl.logits)
+    bufs = moe.moe_a16w4_forward_monolithic(x_dev(wl), logits, *w, topk, renormalize=renorm, block_m=bm, **kw)
+    ids, wts, srt, be, off, npp = moe.moe_route_align(logits, topk, E, bm, renormalize=renorm)
+    torch.cuda.synchronize()
+    for name, got, want in (("ids", bufs.ids, ids), ("weights", bufs.weights, wts), ("sorted_ids", bufs.sorted_ids, srt),
+                            ("block_expert", bufs.block_expert, be), ("expert_offsets", bufs.expert_offsets, off),
+                            ("num_post_pad", bufs.num_post_pad, npp)):
+        assert torch.equal(got.view(torch.int32), want.view(torch.int32)), name
+    if bm <= 32:
+        # one token: the two calls take the same GEMV kernels (64-row blocks
+        # go to other kernels there), so the outputs are bit-identical
+        two = moe.moe_a16w4_forward(x_dev(wl), *w, ids, wts, srt, be, npp, bm, **kw)
+        torch.cuda.synchronize()
+        assert torch.equal(bufs.out.view(torch.int16), two.view(torch.int16))
+    rids, rw = oracle.route_topk(wl.logits, topk, renormalize=renorm)
+    ref = oracle.moe_forward(wl.x, wl.w13, wl.w13_scale, wl.w2, wl.w2_scale, 0, rids, rw, I=I,
+                             w13_bias=b13, w2_bias=b2, swiglu_limit=100.0 if bias else 0.0)
+    check_close(out_f64(bufs.out), ref, f"monolithic T={T} H={H} I={I} E={E} k={topk} bm={bm} renorm={renorm} bias={bias}")
+
+
+def test_forward_monolithic_stages_and_replay(moe):
+    """The monolithic call split into its two stage groups equals the whole
+    call bit for bit, and so does every replay of it captured in a graph."""
+    wl = synth.small(T=1, H=1024, I=512, E=32, topk=6, seed=5, scale_lo=118, scale_hi=128)
+    w = weights_dev(wl)
+    x, logits = x_dev(wl), dev(wl.logits)
+    whole = moe.moe_a16w4_forward_monolithic(x, logits, *w, 6)
+    torch.cuda.synchronize()
+    ref = whole.out.clone()
+    bufs = moe.MonolithicBuffers(1, 1024, 512, 32, 6, 16, x.device)
+    moe.moe_a16w4_forward_monolithic(x, logits, *w, 6, bufs=bufs, stages=moe.MOE_STAGE_GATE_UP)
+    moe.moe_a16w4_forward_monolithic(x, logits, *w, 6, bufs=bufs,
+                                     stages=moe.MOE_STAGE_DOWN | moe.MOE_STAGE_COMBINE)
+    torch.cuda.synchronize()
+    assert torch.equal(bufs.out.view(torch.int16), ref.view(torch.int16))
+    with pytest.raises(moe.MoeError, match="stage mask"):
+        moe.moe_a16w4_forward_monolithic(x, logits, *w, 6, bufs=bufs, stages=moe.MOE_STAGE_DOWN)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        moe.moe_a16w4_forward_monolithic(x, logits, *w, 6, bufs=bufs)
+    torch.cuda.current_stream().wait_stream(side)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        moe.moe_a16w4_forward_monolithic(x, logits, *w, 6, bufs=bufs)
+    for r in range(4):
+        bufs.out.zero_()
+        bufs.workspace.zero_()
+        bufs.ids.fill_(-1)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(bufs.out.view(torch.int16), ref.view(torch.int16)), f"replay {r}"
+        assert torch.equal(bufs.ids, whole.ids)
+
+
 def test_layer_on_side_stream_matches_default_stream(moe):
     """stream= on a side stream: the call's own temporaries are allocated on
     that stream; the output equals the default-stream result bit for bit,
