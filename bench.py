@@ -21,7 +21,8 @@ measured for the same kernel sources (profiles/traffic.json), else null.
 (routing + align/sort + gate_up; down + combine), with events between the
 launches, so it includes launch gaps. `warm` repeats one weight set every
 step (the cold headline rotates over --sets). Prefill lines also carry the
-shader clock sampled under the MFMA load and the peak at that clock. For the int4 workloads `requant` is the load-time
+shader clock under the MFMA load (from the committed SQ-counter profile) and
+the peak at that clock. For the int4 workloads `requant` is the load-time
 MXFP4 -> int4-g32 conversion of one weight set (every expert of w13 and w2, 8
 experts per call into preallocated outputs): bytes read + written per pass
 over its duration, against HBM peak. `cpu_baseline` is the CPU oracle on a
@@ -169,6 +170,18 @@ def stage1_launch_us(layers, moe, eager, fused_t1, reps=4):
     return e0.elapsed_time(e1) * 1e3 / (3 * n)
 
 
+def counter_clock_ghz(workload):
+    """Shader clock under the MFMA load of the dominant prefill kernel, from
+    the committed SQ-counter profile (profiles/sclk.json: SQ_BUSY_CYCLES per
+    shader engine over the kernel's rocprofv3 duration). None without one."""
+    path = os.path.join(ROOT, "profiles", "sclk.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f).get(workload)
+    return rec if rec and rec.get("ghz") else None
+
+
 def measured_traffic(workload, kernel):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
     summary (FETCH_SIZE and WRITE_SIZE, each scaled by the same counter's
@@ -299,40 +312,6 @@ def cpu_baseline(wl, spec, seconds, fmt_name):
                       f"workload, weight set 0"}
 
 
-def sampled_sclk_mhz(run_for_s, work):
-    """Shader clock while `work` keeps the GPU busy: rocm-smi's current sclk,
-    sampled by a child process every ~0.2 s over run_for_s seconds of
-    back-to-back work. None when rocm-smi gives no reading."""
-    import re
-    import subprocess
-    import threading
-
-    import torch
-    samples, stop = [], threading.Event()
-
-    def sampler():
-        while not stop.is_set():
-            try:
-                r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=5)
-                m = re.search(r"sclk.*?\((\d+)\s*Mhz\)", r.stdout, flags=re.I)
-                if m:
-                    samples.append(int(m.group(1)))
-            except Exception:
-                return
-            stop.wait(0.2)
-
-    th = threading.Thread(target=sampler, daemon=True)
-    th.start()
-    t0 = time.perf_counter()
-    while time.perf_counter() - t0 < run_for_s:
-        for _ in range(20):
-            work()
-        torch.cuda.synchronize()
-    stop.set()
-    th.join(timeout=10)
-    return sorted(samples)[len(samples) // 2] if samples else None
-
-
 def main():
     args = parse()
     if args.gpus != 1:
@@ -458,14 +437,15 @@ def main():
         ach = stage1_flops / s1_sec / 1e12
         roof = {"bound": "mfma", "achieved": round(ach, 2), "peak": BF16_MFMA_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(ach / BF16_MFMA_PEAK_TFLOPS, 4), "traffic": None}
-        # The published peak is quoted at 2.4 GHz; the clock the chip holds
-        # under this MFMA load (rocm-smi's sclk while the step replays) gives
-        # the peak the kernel can reach here.
-        work = graphs[0].replay if graphs is not None else layers[0].step
-        mhz = sampled_sclk_mhz(1.5, work)
-        if mhz:
-            at_clock = BF16_MFMA_PEAK_TFLOPS * mhz / 2400.0
-            roof["sclk_mhz_observed"] = mhz
+        # The published peak is quoted at 2.4 GHz. The shader clock this kernel
+        # runs at comes from the committed rocprofv3 SQ counters of the same
+        # kernel (busy cycles per shader engine over its duration); with it,
+        # the peak at that clock.
+        clk = counter_clock_ghz(args.workload)
+        if clk:
+            at_clock = BF16_MFMA_PEAK_TFLOPS * clk["ghz"] / 2.4
+            roof["sclk_ghz_from_counters"] = clk["ghz"]
+            roof["sclk_source"] = clk["source"]
             roof["peak_at_observed_clock"] = round(at_clock, 1)
             roof["frac_at_observed_clock"] = round(ach / at_clock, 4)
     else:
