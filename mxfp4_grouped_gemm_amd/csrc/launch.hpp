@@ -91,8 +91,6 @@ bool prefill_eligible(const MoeGemmArgs& a);
 int64_t prefill_list_bytes(int64_t cap);
 hipError_t launch_prefill(const MoeGemmArgs& a, int stage, void* list_ws, hipStream_t s);
 
-// out[t] = sum_j weight[t, j] * (y[t*topk + j] + w2_bias[ids[t, j]]) (no
-// bias term when w2_bias is null).
 // The layer for one token, router logits in: routing inside the gate_up
 // launch, then down and combine. stages: bit 0 routing + gate_up, bit 1
 // down + combine.
@@ -101,6 +99,8 @@ hipError_t launch_t1_layer(const MoeGemmArgs& a, const float* logits, int renorm
                            float* topk_weights, int32_t* sorted_ids, int32_t* block_expert,
                            int32_t* expert_offsets, int32_t* num_post_pad, unsigned stages, hipStream_t s);
 
+// out[t] = sum_j weight[t, j] * (y[t*topk + j] + w2_bias[ids[t, j]]) (no
+// bias term when w2_bias is null).
 hipError_t launch_combine(const float* y, const int32_t* ids, const float* weights,
                           const uint16_t* w2_bias, int T, int H, int E, int topk, uint16_t* out,
                           hipStream_t s);
