@@ -213,10 +213,13 @@ def fused_t1(T, fmt, H, I, topk, E):
 
 def stage1_kernel_name(T, bm, fmt, H, I, topk, E):
     """Which gate_up kernel the library launches for this shape (the rule of
-    gemv_eligible / forward_stages in the C sources, restated for the label)."""
+    gemv_mfma_eligible / gemv_eligible / forward_stages in the C sources, restated for the label)."""
     if fused_t1(T, fmt, H, I, topk, E):
         return "route_gate_up_t1_kernel"
     rows = min(T, bm)
+    if (bm == 16 and fmt == 0 and rows > 1 and H <= 4096 and I <= 4096
+            and H % 64 == 0 and I % 64 == 0):
+        return "stage1_gemv_mfma_kernel"
     if (bm <= 32 and fmt == 0 and rows <= 8 and H <= 4096 and I <= 4096
             and H % 256 == 0 and I % 128 == 0):
         return "stage1_gemv_kernel"

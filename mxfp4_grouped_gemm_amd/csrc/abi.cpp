@@ -220,7 +220,11 @@ int64_t moe_align_sort_capacity(int T, int topk, int E, int block_m) {
 int moe_default_block_m(int T, int topk, int E) {
     (void)topk;
     (void)E;
-    if (T <= 8) return 16;
+    // 16-row blocks on the matrix-core GEMV kernels up to 12 tokens (T = 12:
+    // gate_up 191 against 218 us on the 32-row tiles); from 16 tokens the
+    // skewed routings, whose hot experts take four passes over their weights
+    // in 16-row blocks, run faster on the 32-row tiles (237 against 198 us).
+    if (T <= 12) return 16;
     return 32;
 }
 

@@ -298,6 +298,8 @@ static hipError_t launch_decode_fmt(const MoeGemmArgs& a, int stage, hipStream_t
 }
 
 hipError_t launch_decode_stage(const MoeGemmArgs& a, int stage, hipStream_t s) {
+    const int rows = a.T < a.bm ? a.T : a.bm;
+    if (rows > 1 && gemv_mfma_eligible(a)) return launch_gemv_mfma_stage(a, stage, s);
     if (gemv_eligible(a)) return launch_gemv_stage(a, stage, s);
     return a.fmt == kFmtMxfp4 ? launch_decode_fmt<kFmtMxfp4>(a, stage, s)
                               : launch_decode_fmt<kFmtInt4g32>(a, stage, s);

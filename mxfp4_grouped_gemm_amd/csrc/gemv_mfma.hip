@@ -1,0 +1,319 @@
+// Decode GEMMs for expert blocks of 2-16 token rows (MXFP4 weights) whose
+// multiply-adds run on the matrix core: v_mfma_f32_4x4x4_16b_bf16, sixteen
+// independent 4x4x4 products per instruction.
+//
+// The GEMV kernels (gemm_gemv.hip) dot every decoded weight with each token
+// row on the VALU: 16 v_dot2 per 16 code bytes per row, so from about four
+// rows per block the VALU, not HBM, sets their pace. Here lane 4b + r holds
+// MX block b of weight row r (16 code bytes, one e8m0 scale) and the same K
+// range of token row r; the sixteen 4x4 products of one MFMA are the sixteen
+// K segments b of a 4-row x 4-token product, each over 4 K elements, so 8
+// MFMAs consume one 16-byte code load for 4 tokens and the K segments are
+// summed across lanes once per unit. The VALU keeps only the decode.
+//
+// A wave owns 16 weight rows (four sets of 4) over the whole K and 4 token
+// rows (a token group) of one expert block; the activation fragments of a K
+// chunk (16 MX blocks) feed all four row sets, so a chunk is 4 code loads +
+// 4 activation loads of 1 KB. Chunks stream through a register ring of depth
+// D (codes and activations of a chunk issued together; vector loads complete
+// in order). The rows' e8m0 bytes go through wave-private LDS. A block of
+// more than 4 rows takes its token groups one after another, each a further
+// pass over the same weights.
+// Stage 1 takes gate columns i0 .. i0+7 and the matching up columns (row set
+// s = gate 2s, gate 2s+1, up 2s, up 2s+1), so SwiGLU is formed in registers;
+// stage 2 takes 16 consecutive rows of w2. h and y are stored by pair index,
+// as on the GEMV path, and the combine kernel follows.
+#include "gemv.hpp"
+
+namespace moe {
+
+constexpr int kGmWaves = 4;  // waves per workgroup: four units of one block
+constexpr int kGmSets = 4;   // row sets of 4 weight rows per wave
+
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mfma4x4(bf16x4_t a, bf16x4_t b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(a, b, c, 0, 0, 0);
+}
+
+// Sum over the 16 lanes 4b + j (b = 0..15) of each j; every lane gets its j's
+// total. Rotations by 4 and 8 within 16-lane rows, then the two row swaps.
+__device__ __forceinline__ float seg_sum(float v) {
+    v = ror_add<0x124>(v);  // row_ror:4
+    v = ror_add<0x128>(v);  // row_ror:8
+    float o = v;
+    permlane16_swap(v, o);
+    v += o;
+    o = v;
+    permlane32_swap(v, o);
+    return v + o;
+}
+
+struct GmSlot {
+    u32x4 w[kGmSets];  // 16 code bytes of this lane's row in each row set
+    u32x4 x[4];        // 64 activation bytes of this lane's token
+};
+
+// One unit: 16 weight rows of one expert over K (nblk MX blocks in NCH
+// chunks of 16) against the token rows of x_off (kOob: no row), acc[s] +=
+// partial sums. w_off[s]: byte offset of this lane's row of set s in rw;
+// lrow[s]: its row in the wave's LDS scale table (nblk bytes per row). Fully
+// unrolled over the chunks, without branches.
+template <int D, int NCH>
+__device__ __forceinline__ void gm_k_loop(rsrc_t rw, rsrc_t rx, uint32_t (&w_off)[kGmSets], uint32_t x_off,
+                                          const uint8_t* lds_scale, int (&lrow)[kGmSets], int nblk, int seg,
+                                          f32x4 (&acc)[kGmSets]) {
+    // Opaque to the optimizer from here: when a block's token groups run this
+    // loop one after another, the per-chunk offsets are then recomputed in
+    // each pass rather than kept live across passes (44 VGPRs).
+#pragma unroll
+    for (int s = 0; s < kGmSets; ++s) asm volatile("" : "+v"(w_off[s]), "+v"(lrow[s]));
+    asm volatile("" : "+v"(seg));
+    GmSlot ring[D];
+    // Blocks past nblk (the last chunk's) load zeros without memory traffic:
+    // an offset with bit 31 set is past every record.
+    auto issue = [&](GmSlot& r, int c) {
+        const uint32_t oob = (uint32_t)(16 * c + seg >= nblk) << 31;
+#pragma unroll
+        for (int s = 0; s < kGmSets; ++s) r.w[s] = bld16nt(rw, (w_off[s] + 256u * c) | oob);
+        const uint32_t o = (x_off + 1024u * c) | oob;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) r.x[q] = bld16(rx, o + 16u * q);
+    };
+    auto consume = [&](const GmSlot& r, int c) {
+        const int blk = min(16 * c + seg, nblk - 1);
+        float sc[kGmSets];
+#pragma unroll
+        for (int s = 0; s < kGmSets; ++s) sc[s] = e8m0_scale_operand(lds_scale[lrow[s] * nblk + blk]);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            bf16x8 wv[kGmSets];
+#pragma unroll
+            for (int s = 0; s < kGmSets; ++s) wv[s] = mxfp4x8_to_bf16(r.w[s][q], sc[s]);
+            const bf16x8 xv = __builtin_bit_cast(bf16x8, r.x[q]);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const bf16x4_t xb = h ? __builtin_shufflevector(xv, xv, 4, 5, 6, 7)
+                                      : __builtin_shufflevector(xv, xv, 0, 1, 2, 3);
+#pragma unroll
+                for (int s = 0; s < kGmSets; ++s) {
+                    const bf16x4_t wb = h ? __builtin_shufflevector(wv[s], wv[s], 4, 5, 6, 7)
+                                          : __builtin_shufflevector(wv[s], wv[s], 0, 1, 2, 3);
+                    acc[s] = mfma4x4(wb, xb, acc[s]);
+                }
+            }
+        }
+    };
+    // The scheduling barriers keep each chunk's loads where they are issued:
+    // left free, the scheduler sinks them next to their first use (fewer live
+    // registers, but one memory round trip per chunk).
+#pragma unroll
+    for (int c = 0; c < D && c < NCH; ++c) issue(ring[c], c);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+        consume(ring[c % D], c);
+        if (c + D < NCH) issue(ring[c % D], c + D);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// The rows' scale bytes into wave-private LDS: run 0 (rows first0 ..
+// first0 + n0 - 1) then run 1 (first1 ..), 16 rows in all, nblk bytes each,
+// as 16-byte pieces (n0 * nblk and 16 * nblk multiples of 16).
+__device__ __forceinline__ void gm_stage_scales(rsrc_t rs, int first0, int n0, int first1, int nblk,
+                                                uint8_t* lds, int lane) {
+    const int p0 = n0 * nblk / 16, ptot = 16 * nblk / 16;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const int p = lane + 64 * k;
+        uint32_t so = kOob;
+        if (p < p0)
+            so = (uint32_t)first0 * nblk + 16u * p;
+        else if (p < ptot)
+            so = (uint32_t)first1 * nblk + 16u * (p - p0);
+        const u32x4 v = bld16nt(rs, so);
+        if (p < ptot) *(u32x4*)(lds + 16 * p) = v;
+    }
+    wave_lds_sync();
+}
+
+// Row sets after seg_sum: acc[s][i] (row slot i of set s) for this lane's
+// token j = lane & 3.
+__device__ __forceinline__ void gm_reduce(f32x4 (&acc)[kGmSets]) {
+#pragma unroll
+    for (int s = 0; s < kGmSets; ++s)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[s][i] = seg_sum(acc[s][i]);
+}
+
+// This lane's block row 4 tg + (lane & 3): its pair, or -1. False when the
+// token group holds no pair (rows are valid-first, so later groups neither).
+__device__ __forceinline__ bool gm_rows(const MoeGemmArgs& a, int64_t row0, int tg, int r, int& pair) {
+    const int P = a.T * a.topk;
+    const int p = a.sorted_ids[row0 + 4 * tg + r];
+    const bool ok = p >= 0 && p < P;
+    pair = ok ? p : -1;
+    return __builtin_amdgcn_ballot_w64(ok) != 0;
+}
+
+// Stage 1: unit u = (expert block b, gate columns i0 .. i0+7 and the matching
+// up columns); the block's token groups one after another.
+template <int D, int NCH, bool EPI>
+__global__ __launch_bounds__(kGmWaves * 64) __attribute__((amdgpu_waves_per_eu(4))) void stage1_gemv_mfma_kernel(MoeGemmArgs a, int ngroups) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds_scale[kGmWaves][16 * 128];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int H = a.H, I = a.I, nblk = H / 32;
+    const int upb = I / 8;
+    const int64_t u = (int64_t)blockIdx.x * kGmWaves + wave;
+    const int64_t b = u / upb;
+    if (b >= a.cap / a.bm) return;
+    const int64_t row0 = b * a.bm;
+    if (row0 >= (int64_t)*a.num_post_pad) return;
+    const int e = a.block_expert[b];
+    if ((unsigned)e >= (unsigned)a.E) return;
+    const int i0 = (int)(u % upb) * 8;
+    const int seg = lane >> 2, r = lane & 3;
+    const int64_t slab_rows = 2 * (int64_t)I;
+    const rsrc_t rw = make_rsrc(a.w13 + e * slab_rows * (H / 2), (uint32_t)(slab_rows * (H / 2)));
+    const rsrc_t rs = make_rsrc((const uint8_t*)a.w13_scale + e * slab_rows * nblk, (uint32_t)(slab_rows * nblk));
+    const rsrc_t rx = make_rsrc(a.x, (uint32_t)((int64_t)a.T * H * 2));
+    uint8_t* lds = lds_scale[wave];
+    gm_stage_scales(rs, i0, 8, I + i0, nblk, lds, lane);
+
+    // Row slot r of set s: gate i0 + 2s + r (r < 2), up i0 + 2s + r - 2.
+    uint32_t w_off[kGmSets];
+    int lrow[kGmSets];
+#pragma unroll
+    for (int s = 0; s < kGmSets; ++s) {
+        const int row = r < 2 ? i0 + 2 * s + r : I + i0 + 2 * s + (r - 2);
+        w_off[s] = (uint32_t)row * (uint32_t)(H / 2) + 16u * seg;
+        lrow[s] = r < 2 ? 2 * s + r : 8 + 2 * s + (r - 2);
+    }
+    // Lane 4c + j with c < 8 stores (token j, column i0 + 2 (c & 3) + (c >> 2)):
+    // gate = row slot c >> 2, up = slot 2 + (c >> 2) of set c & 3.
+    const int sel = seg & 3, half = (seg >> 2) & 1;
+    const int col = i0 + 2 * sel + half;
+    for (int tg = 0; tg < ngroups; ++tg) {
+        int pair;
+        if (!gm_rows(a, row0, tg, r, pair)) break;
+        const uint32_t x_off = pair >= 0 ? (uint32_t)(pair / a.topk) * (uint32_t)(2 * H) + 64u * seg : kOob;
+        f32x4 acc[kGmSets];
+#pragma unroll
+        for (int s = 0; s < kGmSets; ++s) acc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
+        gm_k_loop<D, NCH>(rw, rx, w_off, x_off, lds, lrow, nblk, seg, acc);
+        gm_reduce(acc);
+        float gv = 0.f, uv = 0.f;
+#pragma unroll
+        for (int s = 0; s < kGmSets; ++s) {
+            gv = s == sel ? (half ? acc[s][1] : acc[s][0]) : gv;
+            uv = s == sel ? (half ? acc[s][3] : acc[s][2]) : uv;
+        }
+        if (lane < 32 && pair >= 0) {
+            if constexpr (EPI) {
+                GluTerms glu;
+                glu.load(a, e, col);
+                glu.apply(gv, uv);
+            }
+            a.h[(int64_t)pair * I + col] = f32_to_bf16_bits(swiglu(gv, uv));
+        }
+    }
+}
+
+// Stage 2: unit u = (expert block b, output rows n0 .. n0+15); the block's
+// token groups one after another; y by pair.
+template <int D, int NCH>
+__global__ __launch_bounds__(kGmWaves * 64) __attribute__((amdgpu_waves_per_eu(4))) void stage2_gemv_mfma_kernel(MoeGemmArgs a, int ngroups) {
+    __shared__ __attribute__((aligned(16))) uint8_t lds_scale[kGmWaves][16 * 128];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int H = a.H, I = a.I, nblk = I / 32;
+    const int upb = H / 16;
+    const int64_t u = (int64_t)blockIdx.x * kGmWaves + wave;
+    const int64_t b = u / upb;
+    if (b >= a.cap / a.bm) return;
+    const int64_t row0 = b * a.bm;
+    if (row0 >= (int64_t)*a.num_post_pad) return;
+    const int e = a.block_expert[b];
+    if ((unsigned)e >= (unsigned)a.E) return;
+    const int n0 = (int)(u % upb) * 16;
+    const int seg = lane >> 2, r = lane & 3;
+    const int P = a.T * a.topk;
+
+    const rsrc_t rw = make_rsrc(a.w2 + (int64_t)e * H * (I / 2), (uint32_t)((int64_t)H * (I / 2)));
+    const rsrc_t rs = make_rsrc((const uint8_t*)a.w2_scale + (int64_t)e * H * nblk, (uint32_t)((int64_t)H * nblk));
+    const rsrc_t rx = make_rsrc(a.h, (uint32_t)((int64_t)P * I * 2));
+    uint8_t* lds = lds_scale[wave];
+    gm_stage_scales(rs, n0, 16, n0 + 16, nblk, lds, lane);
+
+    // Row slot r of set s: w2 row n0 + 4s + r.
+    uint32_t w_off[kGmSets];
+    int lrow[kGmSets];
+#pragma unroll
+    for (int s = 0; s < kGmSets; ++s) {
+        w_off[s] = (uint32_t)(n0 + 4 * s + r) * (uint32_t)(I / 2) + 16u * seg;
+        lrow[s] = 4 * s + r;
+    }
+    // Lane 4c + j stores (token j, row n0 + 4 (c & 3) + (c >> 2)).
+    const int sel = seg & 3, slot = seg >> 2;
+    for (int tg = 0; tg < ngroups; ++tg) {
+        int pair;
+        if (!gm_rows(a, row0, tg, r, pair)) break;
+        const uint32_t x_off = pair >= 0 ? (uint32_t)pair * (uint32_t)(2 * I) + 64u * seg : kOob;
+        f32x4 acc[kGmSets];
+#pragma unroll
+        for (int s = 0; s < kGmSets; ++s) acc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
+        gm_k_loop<D, NCH>(rw, rx, w_off, x_off, lds, lrow, nblk, seg, acc);
+        gm_reduce(acc);
+        float v = 0.f;
+#pragma unroll
+        for (int s = 0; s < kGmSets; ++s)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) v = (s == sel && i == slot) ? acc[s][i] : v;
+        if (pair >= 0) a.y[(int64_t)pair * H + n0 + 4 * sel + slot] = v;
+    }
+}
+
+bool gemv_mfma_eligible(const MoeGemmArgs& a) {
+    return a.fmt == kFmtMxfp4 && a.bm == 16 && a.H <= 4096 && a.I <= 4096 && a.H % 64 == 0 &&
+           a.I % 64 == 0 && (int64_t)a.T * a.topk * a.I * 2 < 0x7fff0000LL &&
+           (int64_t)a.T * a.H * 2 < 0x7fff0000LL;
+}
+
+// Chunks in flight per wave: two, with four waves per SIMD (127 VGPRs, no
+// spill). Three chunks with two waves per SIMD were 9-10 % slower at 4 tokens.
+constexpr int kGmDepth = 2;
+
+template <int NCH>
+static void launch_gm_nch(const MoeGemmArgs& a, int stage, int ngroups, dim3 grid, dim3 block, hipStream_t s) {
+    const bool epi = a.w13_bias || a.swiglu_limit > 0.0f;
+    if (stage == 1) {
+        if (epi) hipLaunchKernelGGL((stage1_gemv_mfma_kernel<kGmDepth, NCH, true>), grid, block, 0, s, a, ngroups);
+        else hipLaunchKernelGGL((stage1_gemv_mfma_kernel<kGmDepth, NCH, false>), grid, block, 0, s, a, ngroups);
+    } else {
+        hipLaunchKernelGGL((stage2_gemv_mfma_kernel<kGmDepth, NCH>), grid, block, 0, s, a, ngroups);
+    }
+}
+
+hipError_t launch_gemv_mfma_stage(const MoeGemmArgs& a, int stage, hipStream_t s) {
+    const int64_t nb = a.cap / a.bm;
+    const int64_t units = nb * (stage == 1 ? a.I / 8 : a.H / 16);
+    const int rows = a.T < a.bm ? a.T : a.bm;
+    const int ngroups = (rows + 3) / 4;  // 1..4 token groups of 4 rows
+    const dim3 grid((unsigned)((units + kGmWaves - 1) / kGmWaves)), block(kGmWaves * 64);
+    const int nch = ((stage == 1 ? a.H : a.I) / 32 + 15) / 16;  // 1..8 (K <= 4096)
+    switch (nch) {
+        case 1: launch_gm_nch<1>(a, stage, ngroups, grid, block, s); break;
+        case 2: launch_gm_nch<2>(a, stage, ngroups, grid, block, s); break;
+        case 3: launch_gm_nch<3>(a, stage, ngroups, grid, block, s); break;
+        case 4: launch_gm_nch<4>(a, stage, ngroups, grid, block, s); break;
+        case 5: launch_gm_nch<5>(a, stage, ngroups, grid, block, s); break;
+        case 6: launch_gm_nch<6>(a, stage, ngroups, grid, block, s); break;
+        case 7: launch_gm_nch<7>(a, stage, ngroups, grid, block, s); break;
+        default: launch_gm_nch<8>(a, stage, ngroups, grid, block, s); break;
+    }
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -82,6 +82,11 @@ hipError_t launch_decode_stage(const MoeGemmArgs& a, int stage, hipStream_t s);
 // index.
 bool gemv_eligible(const MoeGemmArgs& a);
 hipError_t launch_gemv_stage(const MoeGemmArgs& a, int stage, hipStream_t s);
+// The same blocks (16 rows, 2-16 of them holding pairs) with the multiply-
+// adds on the matrix core (4x4x4 MFMA products over 16 K segments); MXFP4,
+// H and I multiples of 64 up to 4096.
+bool gemv_mfma_eligible(const MoeGemmArgs& a);
+hipError_t launch_gemv_mfma_stage(const MoeGemmArgs& a, int stage, hipStream_t s);
 
 // LDS-tiled MFMA kernels for prefill sizes (MXFP4, 32-row blocks, H and I
 // multiples of 256). Stage 1 first cuts the sorted blocks into super-blocks

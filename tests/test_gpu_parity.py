@@ -310,6 +310,24 @@ def test_forward_gemv_path_small(moe, T, E, topk, H, I):
     check_close_bf16_out(out_f64(out), ref, f"gemv T={T} E={E} k={topk}")
 
 
+@pytest.mark.parametrize("T,E,topk,H,I", [
+    (12, 16, 4, 512, 1024),   # 5..12 rows per 16-row block: two token groups, two passes
+    (16, 8, 8, 512, 1024),    # topk == E: every block holds all 16 tokens
+    (9, 6, 3, 1280, 640),     # 40 MX blocks: the last 16-block chunk partial
+    (5, 4, 2, 192, 128),      # 6 MX blocks: one partial chunk
+    (3, 3, 3, 4096, 4096),    # largest H and I
+    (2, 40, 20, 2048, 448),   # topk above 16, I a multiple of 64 only
+])
+def test_forward_gemv_mfma_blocks(moe, T, E, topk, H, I):
+    """16-row blocks holding 2-16 token rows take the matrix-core GEMV
+    kernels (4x4x4 MFMA products over 16 K segments); every token compared."""
+    wl = synth.small(T=T, H=H, I=I, E=E, topk=topk, seed=70 + T + H)
+    out = run_layer(moe, wl, topk, bm=16)
+    ids, w = oracle.route_topk(wl.logits, topk)
+    ref = oracle.moe_forward(wl.x, wl.w13, wl.w13_scale, wl.w2, wl.w2_scale, 0, ids, w, I=I)
+    check_close_bf16_out(out_f64(out), ref, f"gemv-mfma T={T} E={E} k={topk} H={H} I={I}")
+
+
 @pytest.mark.parametrize("T,H,I,E,topk,hot", [
     (256, 512, 512, 8, 4, 0),    # ~128 rows per expert: 4-block super-blocks
     (512, 768, 256, 4, 3, 0),    # ~384 rows per expert: two super-blocks each
