@@ -271,6 +271,9 @@ hipError_t launch_route_align(const float* logits, int T, int E, int topk, int r
                               int64_t cap, int32_t* ids, float* weights, int32_t* sorted_ids,
                               int32_t* block_expert, int32_t* expert_offsets, int32_t* num_post_pad,
                               hipStream_t s) {
+    if (route_one_token_eligible(T, E, topk) && cap == (int64_t)topk * bm)
+        return launch_route_one_token(logits, E, topk, renorm, bm, ids, weights, sorted_ids, block_expert,
+                                      expert_offsets, num_post_pad, s);
     const dim3 grid(1), block(kSortThreads);
     const int vpl = (E + 63) / 64;
     const bool small = T <= kSmallTokens && T * topk <= kSmallPairs && cap <= kSmallCapMax;

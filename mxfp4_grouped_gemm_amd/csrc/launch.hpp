@@ -15,6 +15,14 @@ hipError_t launch_align_sort(const int32_t* ids, int P, int E, int bm, int64_t c
                              int32_t* sorted_ids, int32_t* block_expert, int32_t* expert_offsets,
                              int32_t* num_post_pad, hipStream_t s);
 
+// One token over 129-1024 experts (topk <= 64): routing by a whole
+// workgroup; with sorted_ids non-null also the align/sort outputs (capacity
+// topk * bm).
+bool route_one_token_eligible(int T, int E, int topk);
+hipError_t launch_route_one_token(const float* logits, int E, int topk, int renorm, int bm, int32_t* ids,
+                                  float* weights, int32_t* sorted_ids, int32_t* block_expert,
+                                  int32_t* expert_offsets, int32_t* num_post_pad, hipStream_t s);
+
 // Routing and align/sort in one workgroup (T <= 64, T*topk <= 4096).
 bool route_align_fusable(int T, int E, int topk);
 hipError_t launch_route_align(const float* logits, int T, int E, int topk, int renorm, int bm,

@@ -18,6 +18,9 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
 
 hipError_t launch_route_topk(const float* logits, int T, int E, int topk, int renorm, int32_t* ids,
                              float* weights, hipStream_t s) {
+    if (route_one_token_eligible(T, E, topk))
+        return launch_route_one_token(logits, E, topk, renorm, 0, ids, weights, nullptr, nullptr, nullptr,
+                                      nullptr, s);
     const dim3 grid((T + 3) / 4), block(256);
     const int vpl = (E + 63) / 64;
     if (vpl <= 1)

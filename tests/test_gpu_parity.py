@@ -211,11 +211,15 @@ def test_route_align_small_matches_oracle(moe, T, E, topk, bm):
 @pytest.mark.parametrize("E,topk,renorm,ties", [(896, 15, True, False), (1024, 16, True, False),
                                                 (513, 15, True, False), (1000, 1, True, False),
                                                 (896, 15, False, False), (896, 16, True, True),
-                                                (640, 7, False, True), (512, 15, True, False)])
+                                                (640, 7, False, True), (512, 15, True, False),
+                                                (129, 15, True, False), (200, 64, True, True),
+                                                (256, 8, False, False), (1024, 64, False, True),
+                                                (300, 300 // 5, True, True), (130, 130 - 66, False, False)])
 def test_route_align_one_token_many_experts(moe, E, topk, renorm, ties):
-    """One token over more than 512 experts is routed by the whole workgroup
-    (candidates per wave, ranked by one wave): ids and weights equal the
-    single-wave routing of moe_route_topk bit for bit, and the oracle's."""
+    """One token over 129-1024 experts is routed by a whole workgroup (a
+    radix select over 8-bit digits): ids and weights equal the oracle's, and
+    route_align's equal moe_route_topk's bit for bit; the align/sort outputs
+    equal the oracle's."""
     rng = np.random.default_rng(E + topk)
     if ties:
         logits = rng.integers(-3, 4, size=(1, E)).astype(np.float32)
@@ -223,11 +227,16 @@ def test_route_align_one_token_many_experts(moe, E, topk, renorm, ties):
         logits = rng.standard_normal((1, E)).astype(np.float32) * 2
     ids, w, s, be, off, npp = moe.moe_route_align(dev(logits), topk, E, 16, renormalize=renorm)
     ids1, w1 = moe.moe_route_topk(dev(logits), topk, renormalize=renorm)
+    # The same row as two tokens takes the single-wave routing (one wave per
+    # token): the workgroup routing must match it bit for bit.
+    ids2, w2 = moe.moe_route_topk(dev(np.repeat(logits, 2, axis=0)), topk, renormalize=renorm)
     torch.cuda.synchronize()
     rids, rw = oracle.route_topk(logits, topk, renormalize=renorm)
     assert np.array_equal(ids.cpu().numpy(), rids)
     assert np.array_equal(ids1.cpu().numpy(), rids)
+    assert np.array_equal(ids2.cpu().numpy()[:1], rids)
     assert np.array_equal(w.cpu().numpy().view(np.uint32), w1.cpu().numpy().view(np.uint32))
+    assert np.array_equal(w.cpu().numpy().view(np.uint32), w2.cpu().numpy()[:1].view(np.uint32))
     np.testing.assert_allclose(w.cpu().numpy(), rw, rtol=1e-6, atol=1e-7)
     rs, rbe, roff, rnpp = oracle.align_sort(rids, E, 16)
     assert int(npp.item()) == rnpp
