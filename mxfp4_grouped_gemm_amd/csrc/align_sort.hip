@@ -166,13 +166,6 @@ __global__ __launch_bounds__(kSortThreads) void route_align_kernel(
 // coalesced stores. Same outputs as align_sort_body.
 constexpr int kSmallTokens = 32;        // token bitmasks are 32-bit
 
-// A single token over more than 512 experts is routed by all 16 waves of
-// the small kernel (one wave would hold 9-16 experts per lane): 22 -> 16 us
-// at E = 896. At 257-512 experts the workgroup's extra barriers and the
-// candidate ranking cost as much as they save, so one wave routes.
-__host__ __device__ inline bool route_wg_eligible(int T, int E, int topk) {
-    return T == 1 && E > 512 && E <= 1024 && topk <= 16;
-}
 constexpr int kSmallPairs = 512;
 constexpr int64_t kSmallCapMax = 4096;  // e.g. 480 pairs of 112 experts at block_m 32
 
@@ -197,14 +190,9 @@ __global__ __launch_bounds__(NW * 64) void route_align_small_kernel(
     for (int i = tid; i < E; i += NT) tokens[i] = 0u;
     for (int i = tid; i < ncap; i += NT) srt[i] = P;
     for (int i = tid; i < nblk; i += NT) blk[i] = -1;
-    if (NW == 16 && route_wg_eligible(T, E, topk)) {
-        // One token over many experts: all waves route it together.
-        route_token_wg<VPL, 16>(logits, E, topk, renorm, ids, weights, ids_lds);
-    } else {
-        for (int t = wv; t < T; t += NW)
-            route_token<VPL>(logits + (int64_t)t * E, E, topk, renorm, ids + (int64_t)t * topk,
-                             weights + (int64_t)t * topk, ids_lds + t * topk, rk[wv]);
-    }
+    for (int t = wv; t < T; t += NW)
+        route_token<VPL>(logits + (int64_t)t * E, E, topk, renorm, ids + (int64_t)t * topk,
+                         weights + (int64_t)t * topk, ids_lds + t * topk, rk[wv]);
     __syncthreads();
     for (int p = tid; p < P; p += NT) {
         const int e = ids_lds[p];
@@ -279,7 +267,7 @@ hipError_t launch_route_align(const float* logits, int T, int E, int topk, int r
     const bool small = T <= kSmallTokens && T * topk <= kSmallPairs && cap <= kSmallCapMax;
 #define MOE_LAUNCH_RA(V)                                                                                   \
     do {                                                                                                   \
-        if (small && T <= 4 && !route_wg_eligible(T, E, topk))                                             \
+        if (small && T <= 4)                                                                               \
             hipLaunchKernelGGL((route_align_small_kernel<V, 4>), dim3(1), dim3(256), 0, s, logits, T, E,   \
                                topk, renorm, bm, cap, ids, weights, sorted_ids, block_expert,             \
                                expert_offsets, num_post_pad);                                              \

@@ -12,8 +12,9 @@
 // order-preserving 32-bit keys: 16 rounds of (compare, ballot, popcount) over
 // two key bits find the k-th largest key; keys above it are kept and the
 // ties at it are taken lowest index first; the kept experts are then ranked
-// against each other in a scalar loop of at most topk steps. Above 512
-// experts a single token is routed by a whole workgroup (route_token_wg).
+// against each other in a scalar loop of at most topk steps. A single token
+// over more than 128 experts is routed by a whole workgroup instead
+// (route_t1.hip).
 #pragma once
 
 #include "common.hpp"
@@ -175,177 +176,6 @@ __device__ __forceinline__ void route_token(const float* __restrict__ row, int E
             ids[rank[i]] = e;
             weights[rank[i]] = ex[i] / part;
             if (ids_lds) ids_lds[rank[i]] = e;
-        }
-    }
-}
-
-template <int CTRL>
-__device__ __forceinline__ int ror_min_i32(int v) {
-    const int o = __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
-    return v < o ? v : o;
-}
-
-// Minimum over the wave (all 64 lanes active), as a wave-uniform value.
-__device__ __forceinline__ int wave_min_i32(int v) {
-    v = ror_min_i32<0x128>(v);  // row_ror:8
-    v = ror_min_i32<0x124>(v);  // row_ror:4
-    v = ror_min_i32<0x122>(v);  // row_ror:2
-    v = ror_min_i32<0x121>(v);  // row_ror:1 -- every lane holds its row's minimum
-    int m = __builtin_amdgcn_readlane(v, 0);
-    const int m1 = __builtin_amdgcn_readlane(v, 16), m2 = __builtin_amdgcn_readlane(v, 32),
-              m3 = __builtin_amdgcn_readlane(v, 48);
-    m = m1 < m ? m1 : m;
-    m = m2 < m ? m2 : m;
-    return m3 < m ? m3 : m;
-}
-
-// One token routed by all NW waves of the workgroup, for many experts
-// (E <= 64 * NW, topk <= 16), where one wave would walk VPL = E / 64 slots
-// per lane through every round of its selection. Wave w holds experts
-// 64w .. 64w + 63 (one per lane) and keeps its own top min(topk, 64) as
-// candidates; wave 0 ranks the candidates (largest logit first, ties to the
-// lower index; the global top-k is among them); then the softmax terms are
-// laid out as route_token<VPL> holds them (expert lane + 64 i in slot i of
-// lane `lane`) and summed in the same order, so ids and weights equal
-// route_token<VPL>'s bit for bit. Every wave of the workgroup must call it.
-template <int VPL, int NW>
-__device__ __forceinline__ void route_token_wg(const float* __restrict__ row, int E, int topk, int renorm,
-                                               int32_t* __restrict__ ids, float* __restrict__ weights,
-                                               int32_t* __restrict__ ids_lds) {
-    constexpr int NC = NW * 16;      // candidate slots (at most 16 per wave)
-    constexpr int CV = NC / 64;      // candidate slots per lane in wave 0
-    __shared__ uint32_t ckey[NC];
-    __shared__ int32_t cidx[NC];
-    __shared__ int32_t ccount[NW];
-    __shared__ float exv[64 * VPL];
-    __shared__ int32_t srank[64 * VPL];
-    __shared__ uint32_t skmax;
-    const int lane = threadIdx.x & 63;
-    const int wv = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
-    const int e = 64 * wv + lane;
-    const bool ok = e < E;
-    const float v = ok ? row[e] : 0.0f;
-    const uint32_t k = ok ? route_key(v) : 0u;  // valid keys are >= 1
-    const uint64_t below_me = (1ull << lane) - 1ull;
-    const int kk = topk;                          // <= 16 <= 64
-
-    // 1. This wave's top kk: radix select over one key per lane (two bits a
-    // round), then the ties at the threshold in index (lane) order.
-    uint32_t thr = 0u;
-#pragma unroll
-    for (int bit = 30; bit >= 0; bit -= 2) {
-        const uint32_t c1 = thr | (1u << bit), c2 = thr | (2u << bit), c3 = thr | (3u << bit);
-        const int n1 = __popcll(__builtin_amdgcn_ballot_w64(k >= c1));
-        const int n2 = __popcll(__builtin_amdgcn_ballot_w64(k >= c2));
-        const int n3 = __popcll(__builtin_amdgcn_ballot_w64(k >= c3));
-        thr = n3 >= kk ? c3 : n2 >= kk ? c2 : n1 >= kk ? c1 : thr;
-    }
-    const int above = __popcll(__ballot(ok && k > thr));
-    const uint64_t tm = __ballot(ok && k == thr);
-    const bool csel = (ok && k > thr) || ((tm >> lane) & 1ull && __popcll(tm & below_me) < kk - above);
-    const uint64_t cm = __ballot(csel);
-    if (csel) {
-        const int pos = __popcll(cm & below_me);
-        ckey[16 * wv + pos] = k;
-        cidx[16 * wv + pos] = e;
-    }
-    if (lane == 0) ccount[wv] = __popcll(cm);
-#pragma unroll
-    for (int i = wv; i < VPL; i += NW) srank[lane + 64 * i] = -1;
-    __syncthreads();
-
-    // 2. Wave 0 ranks the candidates.
-    if (wv == 0) {
-        uint32_t key[CV];
-        int idx[CV];
-        bool sel[CV];
-        int rank[CV];
-#pragma unroll
-        for (int i = 0; i < CV; ++i) {
-            const int c = lane + 64 * i, w = c >> 4, j = c & 15;
-            const bool has = j < ccount[w];
-            key[i] = has ? ckey[c] : 0u;
-            idx[i] = has ? cidx[c] : 0x7fffffff;
-            sel[i] = false;
-            rank[i] = 0;
-        }
-        uint32_t t2 = 0u;
-#pragma unroll
-        for (int bit = 30; bit >= 0; bit -= 2) {
-            const uint32_t c1 = t2 | (1u << bit), c2 = t2 | (2u << bit), c3 = t2 | (3u << bit);
-            int n1 = 0, n2 = 0, n3 = 0;
-#pragma unroll
-            for (int i = 0; i < CV; ++i) {
-                n1 += __popcll(__builtin_amdgcn_ballot_w64(key[i] >= c1));
-                n2 += __popcll(__builtin_amdgcn_ballot_w64(key[i] >= c2));
-                n3 += __popcll(__builtin_amdgcn_ballot_w64(key[i] >= c3));
-            }
-            t2 = n3 >= topk ? c3 : n2 >= topk ? c2 : n1 >= topk ? c1 : t2;
-        }
-        int need = topk;
-#pragma unroll
-        for (int i = 0; i < CV; ++i) {
-            sel[i] = key[i] > t2;
-            need -= __popcll(__ballot(sel[i]));
-        }
-        // Ties at the threshold: the lowest expert indices first.
-        while (need > 0) {
-            int mi = 0x7fffffff;
-#pragma unroll
-            for (int i = 0; i < CV; ++i)
-                if (key[i] == t2 && key[i] != 0u && !sel[i] && idx[i] < mi) mi = idx[i];
-            const int gm = wave_min_i32(mi);
-#pragma unroll
-            for (int i = 0; i < CV; ++i)
-                if (key[i] == t2 && key[i] != 0u && !sel[i] && idx[i] == gm) sel[i] = true;
-            --need;
-        }
-        uint32_t kmax = 0u;
-#pragma unroll
-        for (int i = 0; i < CV; ++i) {
-            uint64_t m = __ballot(sel[i]);
-            while (m) {
-                const int src = __ffsll((unsigned long long)m) - 1;
-                m &= m - 1ull;
-                const uint32_t kv = (uint32_t)__builtin_amdgcn_readlane((int)key[i], src);
-                const int iv = __builtin_amdgcn_readlane(idx[i], src);
-                kmax = kv > kmax ? kv : kmax;
-#pragma unroll
-                for (int j = 0; j < CV; ++j) rank[j] += (kv > key[j] || (kv == key[j] && iv < idx[j])) ? 1 : 0;
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < CV; ++i) {
-            if (sel[i]) {
-                srank[idx[i]] = rank[i];
-                ids[rank[i]] = idx[i];
-                if (ids_lds) ids_lds[rank[i]] = idx[i];
-            }
-        }
-        if (lane == 0) skmax = kmax;
-    }
-    __syncthreads();
-
-    // 3. The softmax terms, each where route_token<VPL> holds it.
-    const float lmax = route_key_value(skmax);
-    const float ex = ok ? expf(v - lmax) : 0.0f;
-    const bool summed = renorm ? (ok && srank[e] >= 0) : ok;
-    if (e < 64 * VPL) exv[e] = summed ? ex : 0.0f;
-#pragma unroll
-    for (int i = NW + wv; i < VPL; i += NW) exv[lane + 64 * i] = 0.0f;
-    __syncthreads();
-
-    // 4. Wave 0: per-lane sums in slot order, then the same xor tree.
-    if (wv == 0) {
-        float part = 0.0f;
-#pragma unroll
-        for (int i = 0; i < VPL; ++i) part += exv[lane + 64 * i];
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) part += __shfl_xor(part, off);
-#pragma unroll
-        for (int i = 0; i < VPL; ++i) {
-            const int r = srank[lane + 64 * i];
-            if (r >= 0) weights[r] = exv[lane + 64 * i] / part;
         }
     }
 }
