@@ -220,11 +220,12 @@ int64_t moe_align_sort_capacity(int T, int topk, int E, int block_m) {
 int moe_default_block_m(int T, int topk, int E) {
     (void)topk;
     (void)E;
-    // 16-row blocks on the matrix-core GEMV kernels up to 12 tokens (T = 12:
-    // gate_up 191 against 218 us on the 32-row tiles); from 16 tokens the
-    // skewed routings, whose hot experts take four passes over their weights
-    // in 16-row blocks, run faster on the 32-row tiles (237 against 198 us).
-    if (T <= 12) return 16;
+    // 16-row blocks on the matrix-core GEMV kernels up to 16 tokens (gate_up
+    // at 12 tokens 191 against 218 us on the 32-row tiles, at 16 tokens 216
+    // against 233 with the block's activations shared by the workgroup);
+    // above, the 32-row tiles (32 tokens: 261 us either way, skewed 239
+    // against 285).
+    if (T <= 16) return 16;
     return 32;
 }
 

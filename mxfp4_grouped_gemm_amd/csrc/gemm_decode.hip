@@ -299,6 +299,7 @@ static hipError_t launch_decode_fmt(const MoeGemmArgs& a, int stage, hipStream_t
 
 hipError_t launch_decode_stage(const MoeGemmArgs& a, int stage, hipStream_t s) {
     const int rows = a.T < a.bm ? a.T : a.bm;
+    if (a.T > 12 && gemv_mfma_eligible(a)) return launch_gemv_mfma_x_stage(a, stage, s);
     if (rows > 1 && gemv_mfma_eligible(a)) return launch_gemv_mfma_stage(a, stage, s);
     if (gemv_eligible(a)) return launch_gemv_stage(a, stage, s);
     return a.fmt == kFmtMxfp4 ? launch_decode_fmt<kFmtMxfp4>(a, stage, s)

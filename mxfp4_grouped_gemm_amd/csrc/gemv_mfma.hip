@@ -275,6 +275,175 @@ __global__ __launch_bounds__(kGmWaves * 64) __attribute__((amdgpu_waves_per_eu(4
     }
 }
 
+// ---------------------------------------------------------------------------
+// The same units with the block's activation rows shared by the workgroup
+// (blocks of up to 16 rows: 13-32 tokens). The four waves of a workgroup take
+// four consecutive units of one block, so they need the same activations:
+// each K chunk of the block's 16 rows (512 elements, 16 KB) is staged once in
+// LDS by the whole workgroup (double-buffered, one barrier per chunk), and
+// each wave reads its B operands from there, up to two token groups (8 rows)
+// per pass over the weights. The weights keep the 4-row x 256-byte loads
+// above: reading the same bytes as 16 rows x 64 bytes per instruction (the
+// layout a 16x16x32 MFMA operand needs) took 230 against 177 us at 16 tokens.
+constexpr int kGxRowBytes = 1024 + 16;  // one chunk of one activation row in LDS (padded)
+
+struct GxSlot {
+    u32x4 w[kGmSets];  // 16 code bytes of this lane's row in each row set
+    u32x4 x[4];        // this thread's 64 bytes of the chunk's activation tile
+};
+
+template <int STAGE, int NCH, bool EPI>
+__global__ __launch_bounds__(kGmWaves * 64) void gemv_mfma_x_kernel(MoeGemmArgs a) {
+    constexpr int NTG = 2;  // token groups per pass
+    __shared__ __attribute__((aligned(16))) uint8_t xs[2][16 * kGxRowBytes];
+    __shared__ __attribute__((aligned(16))) uint8_t lds_scale[kGmWaves][16 * 128];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int H = a.H, I = a.I;
+    const int K = STAGE == 1 ? H : I, nblk = K / 32;
+    const int upb = STAGE == 1 ? I / 8 : H / 16;  // a multiple of kGmWaves: one block per workgroup
+    const int64_t u = (int64_t)blockIdx.x * kGmWaves + wave;
+    const int64_t b = u / upb;
+    if (b >= a.cap / a.bm) return;  // everything below is uniform per workgroup
+    const int64_t row0 = b * a.bm;
+    if (row0 >= (int64_t)*a.num_post_pad) return;
+    const int e = a.block_expert[b];
+    if ((unsigned)e >= (unsigned)a.E) return;
+    const int seg = lane >> 2, r = lane & 3;
+    const int P = a.T * a.topk;
+    // Rows of the block holding pairs (valid first).
+    int nvalid;
+    {
+        const int p = a.sorted_ids[row0 + (lane & 15)];
+        nvalid = __popcll(__builtin_amdgcn_ballot_w64(p >= 0 && p < P) & 0xFFFFull);
+    }
+    const int ngroups = (nvalid + 3) / 4;
+
+    const int64_t slab_rows = STAGE == 1 ? 2 * (int64_t)I : (int64_t)H;
+    const rsrc_t rw = make_rsrc((STAGE == 1 ? a.w13 : a.w2) + e * slab_rows * (K / 2), (uint32_t)(slab_rows * (K / 2)));
+    const rsrc_t rs = make_rsrc((const uint8_t*)(STAGE == 1 ? a.w13_scale : a.w2_scale) + e * slab_rows * nblk,
+                                (uint32_t)(slab_rows * nblk));
+    const int c0 = (int)(u % upb) * (STAGE == 1 ? 8 : 16);  // stage 1: columns i0; stage 2: rows n0
+    uint8_t* lds = lds_scale[wave];
+    if (STAGE == 1) gm_stage_scales(rs, c0, 8, I + c0, nblk, lds, lane);
+    else gm_stage_scales(rs, c0, 16, c0 + 16, nblk, lds, lane);
+    uint32_t w_off[kGmSets];
+    int lrow[kGmSets];
+#pragma unroll
+    for (int s = 0; s < kGmSets; ++s) {
+        const int row = STAGE == 1 ? (r < 2 ? c0 + 2 * s + r : I + c0 + 2 * s + (r - 2)) : c0 + 4 * s + r;
+        w_off[s] = (uint32_t)row * (uint32_t)(K / 2) + 16u * seg;
+        lrow[s] = STAGE == 1 ? (r < 2 ? 2 * s + r : 8 + 2 * s + (r - 2)) : 4 * s + r;
+    }
+    // Activation staging: thread tid loads bytes 64 pc .. 64 pc + 63 of the
+    // chunk's slice of block row mr.
+    const int mr = tid >> 4, pc = tid & 15;
+    uint32_t x_row = kOob;
+    {
+        const int p = a.sorted_ids[row0 + mr];
+        if (p >= 0 && p < P) x_row = STAGE == 1 ? (uint32_t)(p / a.topk) * (uint32_t)(2 * H) : (uint32_t)p * (uint32_t)(2 * I);
+    }
+    const rsrc_t rx = STAGE == 1 ? make_rsrc(a.x, (uint32_t)((int64_t)a.T * H * 2))
+                                 : make_rsrc(a.h, (uint32_t)((int64_t)P * I * 2));
+
+    for (int tg0 = 0; tg0 < ngroups; tg0 += NTG) {
+        GxSlot ring[2];
+        // Loads of chunk c; blocks past nblk load zeros without memory traffic.
+        auto issue = [&](GxSlot& sl, int c) {
+            const uint32_t xo = (uint32_t)(512 * c + 32 * pc >= K) << 31;
+            const uint32_t xa = (x_row + 1024u * c + 64u * pc) | xo;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) sl.x[k] = bld16(rx, xa + 16u * k);
+            const uint32_t wo = (uint32_t)(16 * c + seg >= nblk) << 31;
+#pragma unroll
+            for (int s = 0; s < kGmSets; ++s) sl.w[s] = bld16nt(rw, (w_off[s] + 256u * c) | wo);
+        };
+        f32x4 acc[NTG][kGmSets];
+#pragma unroll
+        for (int g = 0; g < NTG; ++g)
+#pragma unroll
+            for (int s = 0; s < kGmSets; ++s) acc[g][s] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const bool two = tg0 + 1 < ngroups;  // uniform: the pass's second token group holds rows
+#pragma unroll
+        for (int c = 0; c < 2 && c < NCH; ++c) issue(ring[c], c);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+            GxSlot& sl = ring[c & 1];
+            uint8_t* xb = xs[c & 1];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) *(u32x4*)(xb + mr * kGxRowBytes + 64 * pc + 16 * k) = sl.x[k];
+            asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+            const int blk = min(16 * c + seg, nblk - 1);
+            float sc[kGmSets];
+#pragma unroll
+            for (int s = 0; s < kGmSets; ++s) sc[s] = e8m0_scale_operand(lds[lrow[s] * nblk + blk]);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                bf16x8 wv[kGmSets];
+#pragma unroll
+                for (int s = 0; s < kGmSets; ++s) wv[s] = mxfp4x8_to_bf16(sl.w[s][q], sc[s]);
+#pragma unroll
+                for (int g = 0; g < NTG; ++g) {
+                    if (g == 1 && !two) break;
+                    // Token 4 (tg0 + g) + r, elements 8q .. 8q + 7 of K segment seg.
+                    const bf16x8 xv = *(const bf16x8*)(xb + (4 * (tg0 + g) + r) * kGxRowBytes + 64 * seg + 16 * q);
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const bf16x4_t xh = h ? __builtin_shufflevector(xv, xv, 4, 5, 6, 7)
+                                              : __builtin_shufflevector(xv, xv, 0, 1, 2, 3);
+#pragma unroll
+                        for (int s = 0; s < kGmSets; ++s) {
+                            const bf16x4_t wb = h ? __builtin_shufflevector(wv[s], wv[s], 4, 5, 6, 7)
+                                                  : __builtin_shufflevector(wv[s], wv[s], 0, 1, 2, 3);
+                            acc[g][s] = mfma4x4(wb, xh, acc[g][s]);
+                        }
+                    }
+                }
+            }
+            if (c + 2 < NCH) issue(sl, c + 2);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int g = 0; g < NTG; ++g) {
+            if (g == 1 && !two) break;
+            gm_reduce(acc[g]);
+            const int m = 4 * (tg0 + g) + r;
+            const int pr = a.sorted_ids[row0 + m];
+            const bool ok = pr >= 0 && pr < P;
+            if constexpr (STAGE == 1) {
+                // Lane 4c + j with c < 8 stores (token j, column i0 + 2 (c & 3) + (c >> 2)).
+                const int sel = seg & 3, half = (seg >> 2) & 1;
+                const int col = c0 + 2 * sel + half;
+                float gv = 0.f, uv = 0.f;
+#pragma unroll
+                for (int s = 0; s < kGmSets; ++s) {
+                    gv = s == sel ? (half ? acc[g][s][1] : acc[g][s][0]) : gv;
+                    uv = s == sel ? (half ? acc[g][s][3] : acc[g][s][2]) : uv;
+                }
+                if (lane < 32 && ok) {
+                    if constexpr (EPI) {
+                        GluTerms glu;
+                        glu.load(a, e, col);
+                        glu.apply(gv, uv);
+                    }
+                    a.h[(int64_t)pr * I + col] = f32_to_bf16_bits(swiglu(gv, uv));
+                }
+            } else {
+                // Lane 4c + j stores (token j, row n0 + 4 (c & 3) + (c >> 2)).
+                const int sel = seg & 3, slot = seg >> 2;
+                float v = 0.f;
+#pragma unroll
+                for (int s = 0; s < kGmSets; ++s)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) v = (s == sel && i == slot) ? acc[g][s][i] : v;
+                if (ok) a.y[(int64_t)pr * H + c0 + 4 * sel + slot] = v;
+            }
+        }
+        __syncthreads();  // the next pass rewrites both activation buffers
+    }
+}
+
 bool gemv_mfma_eligible(const MoeGemmArgs& a) {
     return a.fmt == kFmtMxfp4 && a.bm == 16 && a.H <= 4096 && a.I <= 4096 && a.H % 64 == 0 &&
            a.I % 64 == 0 && (int64_t)a.T * a.topk * a.I * 2 < 0x7fff0000LL &&
@@ -294,6 +463,34 @@ static void launch_gm_nch(const MoeGemmArgs& a, int stage, int ngroups, dim3 gri
     } else {
         hipLaunchKernelGGL((stage2_gemv_mfma_kernel<kGmDepth, NCH>), grid, block, 0, s, a, ngroups);
     }
+}
+
+template <int NCH>
+static void launch_gx_nch(const MoeGemmArgs& a, int stage, dim3 grid, dim3 block, hipStream_t s) {
+    if (stage == 1) {
+        if (a.w13_bias || a.swiglu_limit > 0.0f) hipLaunchKernelGGL((gemv_mfma_x_kernel<1, NCH, true>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((gemv_mfma_x_kernel<1, NCH, false>), grid, block, 0, s, a);
+    } else {
+        hipLaunchKernelGGL((gemv_mfma_x_kernel<2, NCH, false>), grid, block, 0, s, a);
+    }
+}
+
+hipError_t launch_gemv_mfma_x_stage(const MoeGemmArgs& a, int stage, hipStream_t s) {
+    const int64_t nb = a.cap / a.bm;
+    const int64_t units = nb * (stage == 1 ? a.I / 8 : a.H / 16);
+    const dim3 grid((unsigned)(units / kGmWaves)), block(kGmWaves * 64);
+    const int nch = ((stage == 1 ? a.H : a.I) / 32 + 15) / 16;  // 1..8 (K <= 4096)
+    switch (nch) {
+        case 1: launch_gx_nch<1>(a, stage, grid, block, s); break;
+        case 2: launch_gx_nch<2>(a, stage, grid, block, s); break;
+        case 3: launch_gx_nch<3>(a, stage, grid, block, s); break;
+        case 4: launch_gx_nch<4>(a, stage, grid, block, s); break;
+        case 5: launch_gx_nch<5>(a, stage, grid, block, s); break;
+        case 6: launch_gx_nch<6>(a, stage, grid, block, s); break;
+        case 7: launch_gx_nch<7>(a, stage, grid, block, s); break;
+        default: launch_gx_nch<8>(a, stage, grid, block, s); break;
+    }
+    return hipGetLastError();
 }
 
 hipError_t launch_gemv_mfma_stage(const MoeGemmArgs& a, int stage, hipStream_t s) {

@@ -95,6 +95,9 @@ hipError_t launch_gemv_stage(const MoeGemmArgs& a, int stage, hipStream_t s);
 // H and I multiples of 64 up to 4096.
 bool gemv_mfma_eligible(const MoeGemmArgs& a);
 hipError_t launch_gemv_mfma_stage(const MoeGemmArgs& a, int stage, hipStream_t s);
+// The same with the block's activation rows staged once per workgroup in LDS
+// and up to 8 token rows per pass (blocks holding many rows).
+hipError_t launch_gemv_mfma_x_stage(const MoeGemmArgs& a, int stage, hipStream_t s);
 
 // LDS-tiled MFMA kernels for prefill sizes (MXFP4, 32-row blocks, H and I
 // multiples of 256). Stage 1 first cuts the sorted blocks into super-blocks

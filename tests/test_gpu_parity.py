@@ -337,6 +337,26 @@ def test_forward_gemv_mfma_blocks(moe, T, E, topk, H, I):
     check_close_bf16_out(out_f64(out), ref, f"gemv-mfma T={T} E={E} k={topk} H={H} I={I}")
 
 
+@pytest.mark.parametrize("T,E,topk,H,I", [
+    (16, 8, 8, 512, 1024),    # topk == E: every 16-row block full
+    (32, 4, 4, 512, 256),     # 32 rows per expert: two blocks of 16 rows, two passes each
+    (20, 16, 4, 640, 384),    # K = 640: two 512-element chunks (the last partial)
+    (20, 16, 4, 640, 320),    # I = 320: w2's K in one partial chunk
+    (13, 6, 3, 384, 448),     # I = 448: w2's K in one partial chunk
+    (24, 40, 20, 1024, 192),  # topk above 16
+    (17, 3, 3, 4096, 4096),   # largest H and I
+])
+def test_forward_gemv_mfma_shared_x_blocks(moe, T, E, topk, H, I):
+    """From 13 tokens, 16-row blocks take the matrix-core GEMV kernels with
+    the block's activation rows staged once per workgroup in LDS and up to 8
+    token rows per pass over the weights; every token compared."""
+    wl = synth.small(T=T, H=H, I=I, E=E, topk=topk, seed=90 + T + H + I)
+    ids, w = oracle.route_topk(wl.logits, topk)
+    out = run_layer(moe, wl, topk, bm=16)
+    ref = oracle.moe_forward(wl.x, wl.w13, wl.w13_scale, wl.w2, wl.w2_scale, 0, ids, w, I=I)
+    check_close_bf16_out(out_f64(out), ref, f"gemv-mfma-x T={T} E={E} k={topk} H={H} I={I}")
+
+
 @pytest.mark.parametrize("T,H,I,E,topk,hot", [
     (256, 512, 512, 8, 4, 0),    # ~128 rows per expert: 4-block super-blocks
     (512, 768, 256, 4, 3, 0),    # ~384 rows per expert: two super-blocks each
@@ -430,6 +450,7 @@ BIAS_CASES = [
     (6, 512, 1024, 16, 4, None, 0, "bc"),  # GEMV, rows reloaded in sequence
     (2, 512, 1024, 40, 20, None, 0, "bc"), # topk above 16: the combine's slot loop
     (16, 512, 256, 8, 4, 32, 0, "bc"),     # single-wave MFMA tiles (gate_up and down)
+    (16, 512, 256, 8, 4, 16, 0, "bc"),     # 16-row blocks, activations shared by the workgroup
     (24, 512, 256, 12, 3, 32, 1, "bc"),    # int4 single-wave tiles
     (256, 512, 512, 8, 4, None, 0, "bc"),  # 4-wave LDS tiles with super-blocks
     (96, 512, 256, 8, 4, None, 1, "bc"),   # int4 on the 4-wave tiles
