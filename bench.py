@@ -217,9 +217,8 @@ def stage1_kernel_name(T, bm, fmt, H, I, topk, E):
     if fused_t1(T, fmt, H, I, topk, E):
         return "route_gate_up_t1_kernel"
     rows = min(T, bm)
-    if (bm == 16 and fmt == 0 and rows > 1 and H <= 4096 and I <= 4096
-            and H % 64 == 0 and I % 64 == 0):
-        return "gemv_mfma_x_kernel<1>" if T > 12 else "stage1_gemv_mfma_kernel"
+    if (bm == 16 and rows > 1 and H <= 4096 and I <= 4096 and H % 64 == 0 and I % 64 == 0):
+        return "gemv_mfma_x_kernel" if T > 12 else "stage1_gemv_mfma_kernel"
     if (bm <= 32 and fmt == 0 and rows <= 8 and H <= 4096 and I <= 4096
             and H % 256 == 0 and I % 128 == 0):
         return "stage1_gemv_kernel"

@@ -1,6 +1,7 @@
-// Decode GEMMs for expert blocks of 2-16 token rows (MXFP4 weights) whose
-// multiply-adds run on the matrix core: v_mfma_f32_4x4x4_16b_bf16, sixteen
-// independent 4x4x4 products per instruction.
+// Decode GEMMs for expert blocks of 2-16 token rows (MXFP4 or int4-g32
+// weights) whose multiply-adds run on the matrix core:
+// v_mfma_f32_4x4x4_16b_bf16, sixteen independent 4x4x4 products per
+// instruction.
 //
 // The GEMV kernels (gemm_gemv.hip) dot every decoded weight with each token
 // row on the VALU: 16 v_dot2 per 16 code bytes per row, so from about four
@@ -16,9 +17,11 @@
 // chunk (16 MX blocks) feed all four row sets, so a chunk is 4 code loads +
 // 4 activation loads of 1 KB. Chunks stream through a register ring of depth
 // D (codes and activations of a chunk issued together; vector loads complete
-// in order). The rows' e8m0 bytes go through wave-private LDS. A block of
-// more than 4 rows takes its token groups one after another, each a further
-// pass over the same weights.
+// in order). The rows' scales (e8m0 bytes, or the int4 groups' bf16) go
+// through wave-private LDS. A block of more than 4 rows takes its token
+// groups one after another, each a further pass over the same weights. With
+// int4-g32 weights a lane's 16 code bytes are one 32-group of its row, so the
+// products of a chunk are folded per group (gm_int4_fold).
 // Stage 1 takes gate columns i0 .. i0+7 and the matching up columns (row set
 // s = gate 2s, gate 2s+1, up 2s, up 2s+1), so SwiGLU is formed in registers;
 // stage 2 takes 16 consecutive rows of w2. h and y are stored by pair index,
@@ -49,17 +52,37 @@ __device__ __forceinline__ float seg_sum(float v) {
     return v + o;
 }
 
+// The value of lane 4 (lane / 4) + i (the same quad), for every lane.
+template <int I>
+__device__ __forceinline__ float quad_bcast(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x55 * I, 0xF, 0xF, false));
+}
+
+// int4-g32 weights: a lane's 16 code bytes are one 32-group of its row, so
+// the products of a chunk are folded per group. The codes enter as code + 136
+// (exact in bf16; the activations permuted to the codes' element order), xs
+// holds the chunk's activation sums of each token and segment (an MFMA
+// against ones), and acc gains scale * (sum of x (code + 136) - 136 xs), the
+// scale of row slot i coming from lane 4 seg + i.
+__device__ __forceinline__ void gm_int4_fold(const f32x4& t, const f32x4& xs, float sc, f32x4& acc) {
+    const float s0 = quad_bcast<0>(sc), s1 = quad_bcast<1>(sc), s2 = quad_bcast<2>(sc), s3 = quad_bcast<3>(sc);
+    acc[0] = fmaf(fmaf(-136.0f, xs[0], t[0]), s0, acc[0]);
+    acc[1] = fmaf(fmaf(-136.0f, xs[1], t[1]), s1, acc[1]);
+    acc[2] = fmaf(fmaf(-136.0f, xs[2], t[2]), s2, acc[2]);
+    acc[3] = fmaf(fmaf(-136.0f, xs[3], t[3]), s3, acc[3]);
+}
+
 struct GmSlot {
     u32x4 w[kGmSets];  // 16 code bytes of this lane's row in each row set
     u32x4 x[4];        // 64 activation bytes of this lane's token
 };
 
-// One unit: 16 weight rows of one expert over K (nblk MX blocks in NCH
-// chunks of 16) against the token rows of x_off (kOob: no row), acc[s] +=
-// partial sums. w_off[s]: byte offset of this lane's row of set s in rw;
-// lrow[s]: its row in the wave's LDS scale table (nblk bytes per row). Fully
-// unrolled over the chunks, without branches.
-template <int D, int NCH>
+// One unit: 16 weight rows of one expert over K (nblk MX blocks or int4
+// groups in NCH chunks of 16) against the token rows of x_off (kOob: no row),
+// acc[s] += partial sums. w_off[s]: byte offset of this lane's row of set s in
+// rw; lrow[s]: its row in the wave's LDS scale table (nblk scales per row).
+// Fully unrolled over the chunks, without branches.
+template <int FMT, int D, int NCH>
 __device__ __forceinline__ void gm_k_loop(rsrc_t rw, rsrc_t rx, uint32_t (&w_off)[kGmSets], uint32_t x_off,
                                           const uint8_t* lds_scale, int (&lrow)[kGmSets], int nblk, int seg,
                                           f32x4 (&acc)[kGmSets]) {
@@ -82,25 +105,51 @@ __device__ __forceinline__ void gm_k_loop(rsrc_t rw, rsrc_t rx, uint32_t (&w_off
     };
     auto consume = [&](const GmSlot& r, int c) {
         const int blk = min(16 * c + seg, nblk - 1);
-        float sc[kGmSets];
+        if constexpr (FMT == kFmtMxfp4) {
+            float sc[kGmSets];
 #pragma unroll
-        for (int s = 0; s < kGmSets; ++s) sc[s] = e8m0_scale_operand(lds_scale[lrow[s] * nblk + blk]);
+            for (int s = 0; s < kGmSets; ++s) sc[s] = e8m0_scale_operand(lds_scale[lrow[s] * nblk + blk]);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            bf16x8 wv[kGmSets];
+            for (int q = 0; q < 4; ++q) {
+                bf16x8 wv[kGmSets];
 #pragma unroll
-            for (int s = 0; s < kGmSets; ++s) wv[s] = mxfp4x8_to_bf16(r.w[s][q], sc[s]);
-            const bf16x8 xv = __builtin_bit_cast(bf16x8, r.x[q]);
+                for (int s = 0; s < kGmSets; ++s) wv[s] = mxfp4x8_to_bf16(r.w[s][q], sc[s]);
+                const bf16x8 xv = __builtin_bit_cast(bf16x8, r.x[q]);
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const bf16x4_t xb = h ? __builtin_shufflevector(xv, xv, 4, 5, 6, 7)
-                                      : __builtin_shufflevector(xv, xv, 0, 1, 2, 3);
+                for (int h = 0; h < 2; ++h) {
+                    const bf16x4_t xb = h ? __builtin_shufflevector(xv, xv, 4, 5, 6, 7)
+                                          : __builtin_shufflevector(xv, xv, 0, 1, 2, 3);
+#pragma unroll
+                    for (int s = 0; s < kGmSets; ++s) {
+                        const bf16x4_t wb = h ? __builtin_shufflevector(wv[s], wv[s], 4, 5, 6, 7)
+                                              : __builtin_shufflevector(wv[s], wv[s], 0, 1, 2, 3);
+                        acc[s] = mfma4x4(wb, xb, acc[s]);
+                    }
+                }
+            }
+        } else {
+            const bf16x4_t ones = __builtin_bit_cast(bf16x4_t, u32x2{0x3F803F80u, 0x3F803F80u});
+            f32x4 t[kGmSets], xs = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < kGmSets; ++s) t[s] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const bf16x8 xv = perm_x_int4(__builtin_bit_cast(bf16x8, r.x[q]));
+                const bf16x4_t x0 = __builtin_shufflevector(xv, xv, 0, 1, 2, 3);
+                const bf16x4_t x1 = __builtin_shufflevector(xv, xv, 4, 5, 6, 7);
+                xs = mfma4x4(ones, x0, xs);
+                xs = mfma4x4(ones, x1, xs);
 #pragma unroll
                 for (int s = 0; s < kGmSets; ++s) {
-                    const bf16x4_t wb = h ? __builtin_shufflevector(wv[s], wv[s], 4, 5, 6, 7)
-                                          : __builtin_shufflevector(wv[s], wv[s], 0, 1, 2, 3);
-                    acc[s] = mfma4x4(wb, xb, acc[s]);
+                    const bf16x8 wv = int4x8_to_bf16_biased(r.w[s][q]);
+                    t[s] = mfma4x4(__builtin_shufflevector(wv, wv, 0, 1, 2, 3), x0, t[s]);
+                    t[s] = mfma4x4(__builtin_shufflevector(wv, wv, 4, 5, 6, 7), x1, t[s]);
                 }
+            }
+#pragma unroll
+            for (int s = 0; s < kGmSets; ++s) {
+                const uint16_t sb = *(const uint16_t*)(lds_scale + 2 * (lrow[s] * nblk + blk));
+                gm_int4_fold(t[s], xs, bf16_bits_to_f32(sb), acc[s]);
             }
         }
     };
@@ -118,20 +167,21 @@ __device__ __forceinline__ void gm_k_loop(rsrc_t rw, rsrc_t rx, uint32_t (&w_off
     }
 }
 
-// The rows' scale bytes into wave-private LDS: run 0 (rows first0 ..
-// first0 + n0 - 1) then run 1 (first1 ..), 16 rows in all, nblk bytes each,
-// as 16-byte pieces (n0 * nblk and 16 * nblk multiples of 16).
-__device__ __forceinline__ void gm_stage_scales(rsrc_t rs, int first0, int n0, int first1, int nblk,
+// The rows' scales into wave-private LDS: run 0 (rows first0 ..
+// first0 + n0 - 1) then run 1 (first1 ..), 16 rows in all, nblk scales of sb
+// bytes each (e8m0: 1, bf16: 2), as 16-byte pieces (n0 * nblk * sb and
+// 16 * nblk * sb multiples of 16).
+__device__ __forceinline__ void gm_stage_scales(rsrc_t rs, int first0, int n0, int first1, int nblk, int sb,
                                                 uint8_t* lds, int lane) {
-    const int p0 = n0 * nblk / 16, ptot = 16 * nblk / 16;
+    const int rb = nblk * sb, p0 = n0 * rb / 16, ptot = rb;  // 16 rows * rb / 16
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
+    for (int k = 0; k < 4; ++k) {
         const int p = lane + 64 * k;
         uint32_t so = kOob;
         if (p < p0)
-            so = (uint32_t)first0 * nblk + 16u * p;
+            so = (uint32_t)first0 * rb + 16u * p;
         else if (p < ptot)
-            so = (uint32_t)first1 * nblk + 16u * (p - p0);
+            so = (uint32_t)first1 * rb + 16u * (p - p0);
         const u32x4 v = bld16nt(rs, so);
         if (p < ptot) *(u32x4*)(lds + 16 * p) = v;
     }
@@ -159,9 +209,10 @@ __device__ __forceinline__ bool gm_rows(const MoeGemmArgs& a, int64_t row0, int 
 
 // Stage 1: unit u = (expert block b, gate columns i0 .. i0+7 and the matching
 // up columns); the block's token groups one after another.
-template <int D, int NCH, bool EPI>
-__global__ __launch_bounds__(kGmWaves * 64) __attribute__((amdgpu_waves_per_eu(4))) void stage1_gemv_mfma_kernel(MoeGemmArgs a, int ngroups) {
-    __shared__ __attribute__((aligned(16))) uint8_t lds_scale[kGmWaves][16 * 128];
+template <int FMT, int D, int NCH, bool EPI>
+__global__ __launch_bounds__(kGmWaves * 64) __attribute__((amdgpu_waves_per_eu(FMT == kFmtMxfp4 ? 4 : 1))) void stage1_gemv_mfma_kernel(MoeGemmArgs a, int ngroups) {
+    constexpr int SB = FMT == kFmtMxfp4 ? 1 : 2;  // scale bytes
+    __shared__ __attribute__((aligned(16))) uint8_t lds_scale[kGmWaves][16 * 128 * SB];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int H = a.H, I = a.I, nblk = H / 32;
@@ -177,10 +228,10 @@ __global__ __launch_bounds__(kGmWaves * 64) __attribute__((amdgpu_waves_per_eu(4
     const int seg = lane >> 2, r = lane & 3;
     const int64_t slab_rows = 2 * (int64_t)I;
     const rsrc_t rw = make_rsrc(a.w13 + e * slab_rows * (H / 2), (uint32_t)(slab_rows * (H / 2)));
-    const rsrc_t rs = make_rsrc((const uint8_t*)a.w13_scale + e * slab_rows * nblk, (uint32_t)(slab_rows * nblk));
+    const rsrc_t rs = make_rsrc((const uint8_t*)a.w13_scale + e * slab_rows * nblk * SB, (uint32_t)(slab_rows * nblk * SB));
     const rsrc_t rx = make_rsrc(a.x, (uint32_t)((int64_t)a.T * H * 2));
     uint8_t* lds = lds_scale[wave];
-    gm_stage_scales(rs, i0, 8, I + i0, nblk, lds, lane);
+    gm_stage_scales(rs, i0, 8, I + i0, nblk, SB, lds, lane);
 
     // Row slot r of set s: gate i0 + 2s + r (r < 2), up i0 + 2s + r - 2.
     uint32_t w_off[kGmSets];
@@ -202,7 +253,7 @@ __global__ __launch_bounds__(kGmWaves * 64) __attribute__((amdgpu_waves_per_eu(4
         f32x4 acc[kGmSets];
 #pragma unroll
         for (int s = 0; s < kGmSets; ++s) acc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
-        gm_k_loop<D, NCH>(rw, rx, w_off, x_off, lds, lrow, nblk, seg, acc);
+        gm_k_loop<FMT, D, NCH>(rw, rx, w_off, x_off, lds, lrow, nblk, seg, acc);
         gm_reduce(acc);
         float gv = 0.f, uv = 0.f;
 #pragma unroll
@@ -223,9 +274,10 @@ __global__ __launch_bounds__(kGmWaves * 64) __attribute__((amdgpu_waves_per_eu(4
 
 // Stage 2: unit u = (expert block b, output rows n0 .. n0+15); the block's
 // token groups one after another; y by pair.
-template <int D, int NCH>
-__global__ __launch_bounds__(kGmWaves * 64) __attribute__((amdgpu_waves_per_eu(4))) void stage2_gemv_mfma_kernel(MoeGemmArgs a, int ngroups) {
-    __shared__ __attribute__((aligned(16))) uint8_t lds_scale[kGmWaves][16 * 128];
+template <int FMT, int D, int NCH>
+__global__ __launch_bounds__(kGmWaves * 64) __attribute__((amdgpu_waves_per_eu(FMT == kFmtMxfp4 ? 4 : 1))) void stage2_gemv_mfma_kernel(MoeGemmArgs a, int ngroups) {
+    constexpr int SB = FMT == kFmtMxfp4 ? 1 : 2;  // scale bytes
+    __shared__ __attribute__((aligned(16))) uint8_t lds_scale[kGmWaves][16 * 128 * SB];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int H = a.H, I = a.I, nblk = I / 32;
@@ -242,10 +294,10 @@ __global__ __launch_bounds__(kGmWaves * 64) __attribute__((amdgpu_waves_per_eu(4
     const int P = a.T * a.topk;
 
     const rsrc_t rw = make_rsrc(a.w2 + (int64_t)e * H * (I / 2), (uint32_t)((int64_t)H * (I / 2)));
-    const rsrc_t rs = make_rsrc((const uint8_t*)a.w2_scale + (int64_t)e * H * nblk, (uint32_t)((int64_t)H * nblk));
+    const rsrc_t rs = make_rsrc((const uint8_t*)a.w2_scale + (int64_t)e * H * nblk * SB, (uint32_t)((int64_t)H * nblk * SB));
     const rsrc_t rx = make_rsrc(a.h, (uint32_t)((int64_t)P * I * 2));
     uint8_t* lds = lds_scale[wave];
-    gm_stage_scales(rs, n0, 16, n0 + 16, nblk, lds, lane);
+    gm_stage_scales(rs, n0, 16, n0 + 16, nblk, SB, lds, lane);
 
     // Row slot r of set s: w2 row n0 + 4s + r.
     uint32_t w_off[kGmSets];
@@ -264,7 +316,7 @@ __global__ __launch_bounds__(kGmWaves * 64) __attribute__((amdgpu_waves_per_eu(4
         f32x4 acc[kGmSets];
 #pragma unroll
         for (int s = 0; s < kGmSets; ++s) acc[s] = f32x4{0.f, 0.f, 0.f, 0.f};
-        gm_k_loop<D, NCH>(rw, rx, w_off, x_off, lds, lrow, nblk, seg, acc);
+        gm_k_loop<FMT, D, NCH>(rw, rx, w_off, x_off, lds, lrow, nblk, seg, acc);
         gm_reduce(acc);
         float v = 0.f;
 #pragma unroll
@@ -277,7 +329,7 @@ __global__ __launch_bounds__(kGmWaves * 64) __attribute__((amdgpu_waves_per_eu(4
 
 // ---------------------------------------------------------------------------
 // The same units with the block's activation rows shared by the workgroup
-// (blocks of up to 16 rows: 13-32 tokens). The four waves of a workgroup take
+// (blocks of up to 16 rows: 13-16 tokens), MXFP4 or int4-g32. The four waves of a workgroup take
 // four consecutive units of one block, so they need the same activations:
 // each K chunk of the block's 16 rows (512 elements, 16 KB) is staged once in
 // LDS by the whole workgroup (double-buffered, one barrier per chunk), and
@@ -292,11 +344,16 @@ struct GxSlot {
     u32x4 x[4];        // this thread's 64 bytes of the chunk's activation tile
 };
 
-template <int STAGE, int NCH, bool EPI>
-__global__ __launch_bounds__(kGmWaves * 64) void gemv_mfma_x_kernel(MoeGemmArgs a) {
-    constexpr int NTG = 2;  // token groups per pass
+// int4: held to three waves per SIMD (a few spilled registers); its own
+// choice of 200 VGPRs and two waves was 4-15 % slower at 16 tokens.
+template <int FMT, int STAGE, int NCH, bool EPI>
+__global__ __launch_bounds__(kGmWaves * 64) __attribute__((amdgpu_waves_per_eu(FMT == kFmtMxfp4 ? 1 : 3))) void gemv_mfma_x_kernel(MoeGemmArgs a) {
+    // Token groups per pass: two (MXFP4); one for int4, whose per-chunk group
+    // sums take the registers of the second.
+    constexpr int NTG = FMT == kFmtMxfp4 ? 2 : 1;
+    constexpr int SB = FMT == kFmtMxfp4 ? 1 : 2;  // scale bytes
     __shared__ __attribute__((aligned(16))) uint8_t xs[2][16 * kGxRowBytes];
-    __shared__ __attribute__((aligned(16))) uint8_t lds_scale[kGmWaves][16 * 128];
+    __shared__ __attribute__((aligned(16))) uint8_t lds_scale[kGmWaves][16 * 128 * SB];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int H = a.H, I = a.I;
@@ -321,12 +378,12 @@ __global__ __launch_bounds__(kGmWaves * 64) void gemv_mfma_x_kernel(MoeGemmArgs 
 
     const int64_t slab_rows = STAGE == 1 ? 2 * (int64_t)I : (int64_t)H;
     const rsrc_t rw = make_rsrc((STAGE == 1 ? a.w13 : a.w2) + e * slab_rows * (K / 2), (uint32_t)(slab_rows * (K / 2)));
-    const rsrc_t rs = make_rsrc((const uint8_t*)(STAGE == 1 ? a.w13_scale : a.w2_scale) + e * slab_rows * nblk,
-                                (uint32_t)(slab_rows * nblk));
+    const rsrc_t rs = make_rsrc((const uint8_t*)(STAGE == 1 ? a.w13_scale : a.w2_scale) + e * slab_rows * nblk * SB,
+                                (uint32_t)(slab_rows * nblk * SB));
     const int c0 = (int)(u % upb) * (STAGE == 1 ? 8 : 16);  // stage 1: columns i0; stage 2: rows n0
     uint8_t* lds = lds_scale[wave];
-    if (STAGE == 1) gm_stage_scales(rs, c0, 8, I + c0, nblk, lds, lane);
-    else gm_stage_scales(rs, c0, 16, c0 + 16, nblk, lds, lane);
+    if (STAGE == 1) gm_stage_scales(rs, c0, 8, I + c0, nblk, SB, lds, lane);
+    else gm_stage_scales(rs, c0, 16, c0 + 16, nblk, SB, lds, lane);
     uint32_t w_off[kGmSets];
     int lrow[kGmSets];
 #pragma unroll
@@ -375,30 +432,57 @@ __global__ __launch_bounds__(kGmWaves * 64) void gemv_mfma_x_kernel(MoeGemmArgs 
             for (int k = 0; k < 4; ++k) *(u32x4*)(xb + mr * kGxRowBytes + 64 * pc + 16 * k) = sl.x[k];
             asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
             const int blk = min(16 * c + seg, nblk - 1);
-            float sc[kGmSets];
+            if constexpr (FMT == kFmtMxfp4) {
+                float sc[kGmSets];
 #pragma unroll
-            for (int s = 0; s < kGmSets; ++s) sc[s] = e8m0_scale_operand(lds[lrow[s] * nblk + blk]);
+                for (int s = 0; s < kGmSets; ++s) sc[s] = e8m0_scale_operand(lds[lrow[s] * nblk + blk]);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                bf16x8 wv[kGmSets];
+                for (int q = 0; q < 4; ++q) {
+                    bf16x8 wv[kGmSets];
 #pragma unroll
-                for (int s = 0; s < kGmSets; ++s) wv[s] = mxfp4x8_to_bf16(sl.w[s][q], sc[s]);
+                    for (int s = 0; s < kGmSets; ++s) wv[s] = mxfp4x8_to_bf16(sl.w[s][q], sc[s]);
 #pragma unroll
-                for (int g = 0; g < NTG; ++g) {
-                    if (g == 1 && !two) break;
-                    // Token 4 (tg0 + g) + r, elements 8q .. 8q + 7 of K segment seg.
-                    const bf16x8 xv = *(const bf16x8*)(xb + (4 * (tg0 + g) + r) * kGxRowBytes + 64 * seg + 16 * q);
+                    for (int g = 0; g < NTG; ++g) {
+                        if (g == 1 && !two) break;
+                        // Token 4 (tg0 + g) + r, elements 8q .. 8q + 7 of K segment seg.
+                        const bf16x8 xv = *(const bf16x8*)(xb + (4 * (tg0 + g) + r) * kGxRowBytes + 64 * seg + 16 * q);
 #pragma unroll
-                    for (int h = 0; h < 2; ++h) {
-                        const bf16x4_t xh = h ? __builtin_shufflevector(xv, xv, 4, 5, 6, 7)
-                                              : __builtin_shufflevector(xv, xv, 0, 1, 2, 3);
+                        for (int h = 0; h < 2; ++h) {
+                            const bf16x4_t xh = h ? __builtin_shufflevector(xv, xv, 4, 5, 6, 7)
+                                                  : __builtin_shufflevector(xv, xv, 0, 1, 2, 3);
 #pragma unroll
-                        for (int s = 0; s < kGmSets; ++s) {
-                            const bf16x4_t wb = h ? __builtin_shufflevector(wv[s], wv[s], 4, 5, 6, 7)
-                                                  : __builtin_shufflevector(wv[s], wv[s], 0, 1, 2, 3);
-                            acc[g][s] = mfma4x4(wb, xh, acc[g][s]);
+                            for (int s = 0; s < kGmSets; ++s) {
+                                const bf16x4_t wb = h ? __builtin_shufflevector(wv[s], wv[s], 4, 5, 6, 7)
+                                                      : __builtin_shufflevector(wv[s], wv[s], 0, 1, 2, 3);
+                                acc[g][s] = mfma4x4(wb, xh, acc[g][s]);
+                            }
                         }
                     }
+                }
+            } else {  // int4-g32, one token group: fold the chunk per group (gm_int4_fold)
+                const bf16x4_t ones = __builtin_bit_cast(bf16x4_t, u32x2{0x3F803F80u, 0x3F803F80u});
+                f32x4 t[kGmSets], xsum = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < kGmSets; ++s) t[s] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const bf16x8 xv =
+                        perm_x_int4(*(const bf16x8*)(xb + (4 * tg0 + r) * kGxRowBytes + 64 * seg + 16 * q));
+                    const bf16x4_t x0 = __builtin_shufflevector(xv, xv, 0, 1, 2, 3);
+                    const bf16x4_t x1 = __builtin_shufflevector(xv, xv, 4, 5, 6, 7);
+                    xsum = mfma4x4(ones, x0, xsum);
+                    xsum = mfma4x4(ones, x1, xsum);
+#pragma unroll
+                    for (int s = 0; s < kGmSets; ++s) {
+                        const bf16x8 wv = int4x8_to_bf16_biased(sl.w[s][q]);
+                        t[s] = mfma4x4(__builtin_shufflevector(wv, wv, 0, 1, 2, 3), x0, t[s]);
+                        t[s] = mfma4x4(__builtin_shufflevector(wv, wv, 4, 5, 6, 7), x1, t[s]);
+                    }
+                }
+#pragma unroll
+                for (int s = 0; s < kGmSets; ++s) {
+                    const uint16_t sb = *(const uint16_t*)(lds + 2 * (lrow[s] * nblk + blk));
+                    gm_int4_fold(t[s], xsum, bf16_bits_to_f32(sb), acc[0][s]);
                 }
             }
             if (c + 2 < NCH) issue(sl, c + 2);
@@ -445,7 +529,7 @@ __global__ __launch_bounds__(kGmWaves * 64) void gemv_mfma_x_kernel(MoeGemmArgs 
 }
 
 bool gemv_mfma_eligible(const MoeGemmArgs& a) {
-    return a.fmt == kFmtMxfp4 && a.bm == 16 && a.H <= 4096 && a.I <= 4096 && a.H % 64 == 0 &&
+    return (a.fmt == kFmtMxfp4 || a.fmt == kFmtInt4g32) && a.bm == 16 && a.H <= 4096 && a.I <= 4096 && a.H % 64 == 0 &&
            a.I % 64 == 0 && (int64_t)a.T * a.topk * a.I * 2 < 0x7fff0000LL &&
            (int64_t)a.T * a.H * 2 < 0x7fff0000LL;
 }
@@ -454,25 +538,37 @@ bool gemv_mfma_eligible(const MoeGemmArgs& a) {
 // spill). Three chunks with two waves per SIMD were 9-10 % slower at 4 tokens.
 constexpr int kGmDepth = 2;
 
-template <int NCH>
+template <int FMT, int NCH>
 static void launch_gm_nch(const MoeGemmArgs& a, int stage, int ngroups, dim3 grid, dim3 block, hipStream_t s) {
     const bool epi = a.w13_bias || a.swiglu_limit > 0.0f;
     if (stage == 1) {
-        if (epi) hipLaunchKernelGGL((stage1_gemv_mfma_kernel<kGmDepth, NCH, true>), grid, block, 0, s, a, ngroups);
-        else hipLaunchKernelGGL((stage1_gemv_mfma_kernel<kGmDepth, NCH, false>), grid, block, 0, s, a, ngroups);
+        if (epi) hipLaunchKernelGGL((stage1_gemv_mfma_kernel<FMT, kGmDepth, NCH, true>), grid, block, 0, s, a, ngroups);
+        else hipLaunchKernelGGL((stage1_gemv_mfma_kernel<FMT, kGmDepth, NCH, false>), grid, block, 0, s, a, ngroups);
     } else {
-        hipLaunchKernelGGL((stage2_gemv_mfma_kernel<kGmDepth, NCH>), grid, block, 0, s, a, ngroups);
+        hipLaunchKernelGGL((stage2_gemv_mfma_kernel<FMT, kGmDepth, NCH>), grid, block, 0, s, a, ngroups);
+    }
+}
+
+template <int NCH>
+static void launch_gm_nch(const MoeGemmArgs& a, int stage, int ngroups, dim3 grid, dim3 block, hipStream_t s) {
+    if (a.fmt == kFmtMxfp4) launch_gm_nch<kFmtMxfp4, NCH>(a, stage, ngroups, grid, block, s);
+    else launch_gm_nch<kFmtInt4g32, NCH>(a, stage, ngroups, grid, block, s);
+}
+
+template <int FMT, int NCH>
+static void launch_gx_nch(const MoeGemmArgs& a, int stage, dim3 grid, dim3 block, hipStream_t s) {
+    if (stage == 1) {
+        if (a.w13_bias || a.swiglu_limit > 0.0f) hipLaunchKernelGGL((gemv_mfma_x_kernel<FMT, 1, NCH, true>), grid, block, 0, s, a);
+        else hipLaunchKernelGGL((gemv_mfma_x_kernel<FMT, 1, NCH, false>), grid, block, 0, s, a);
+    } else {
+        hipLaunchKernelGGL((gemv_mfma_x_kernel<FMT, 2, NCH, false>), grid, block, 0, s, a);
     }
 }
 
 template <int NCH>
 static void launch_gx_nch(const MoeGemmArgs& a, int stage, dim3 grid, dim3 block, hipStream_t s) {
-    if (stage == 1) {
-        if (a.w13_bias || a.swiglu_limit > 0.0f) hipLaunchKernelGGL((gemv_mfma_x_kernel<1, NCH, true>), grid, block, 0, s, a);
-        else hipLaunchKernelGGL((gemv_mfma_x_kernel<1, NCH, false>), grid, block, 0, s, a);
-    } else {
-        hipLaunchKernelGGL((gemv_mfma_x_kernel<2, NCH, false>), grid, block, 0, s, a);
-    }
+    if (a.fmt == kFmtMxfp4) launch_gx_nch<kFmtMxfp4, NCH>(a, stage, grid, block, s);
+    else launch_gx_nch<kFmtInt4g32, NCH>(a, stage, grid, block, s);
 }
 
 hipError_t launch_gemv_mfma_x_stage(const MoeGemmArgs& a, int stage, hipStream_t s) {

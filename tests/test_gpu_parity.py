@@ -357,6 +357,33 @@ def test_forward_gemv_mfma_shared_x_blocks(moe, T, E, topk, H, I):
     check_close_bf16_out(out_f64(out), ref, f"gemv-mfma-x T={T} E={E} k={topk} H={H} I={I}")
 
 
+@pytest.mark.parametrize("T,E,topk,H,I,bias", [
+    (3, 8, 4, 512, 256, False),     # 2-4 rows: one token group, one pass
+    (8, 4, 3, 640, 384, False),     # up to 8 rows: two passes; partial last chunk (K = 640)
+    (14, 6, 3, 512, 1024, False),   # activations shared by the workgroup
+    (16, 4, 4, 768, 512, True),     # every block full; biases and the clamp
+])
+def test_forward_gemv_mfma_int4(moe, T, E, topk, H, I, bias):
+    """int4-g32 weights on the matrix-core GEMV kernels (16-row blocks): per
+    32-group fold of code + 136 products, the group's bf16 scale and the
+    activation sums; every token compared with the oracle's int4 forward."""
+    wl = synth.small(T=T, H=H, I=I, E=E, topk=topk, seed=150 + T + H)
+    q13, s13 = moe.requantize_mxfp4_experts(dev(wl.w13), dev(wl.w13_scale))
+    q2, s2 = moe.requantize_mxfp4_experts(dev(wl.w2), dev(wl.w2_scale))
+    r13, rs13 = oracle.requant_int4g32(wl.w13, wl.w13_scale)
+    r2, rs2 = oracle.requant_int4g32(wl.w2, wl.w2_scale)
+    ids, w = oracle.route_topk(wl.logits, topk)
+    kw = {}
+    if bias:
+        b13, b2 = synth.biases(E, H, I, seed=T + E)
+        kw = dict(w13_bias=b13, w2_bias=b2, swiglu_limit=100.0)
+    out = moe.moe_a16w4_layer(x_dev(wl), dev(wl.logits), q13, s13, q2, s2, topk, fmt=1, block_m=16,
+                              **{k: (dev(v, torch.bfloat16) if k != "swiglu_limit" else v) for k, v in kw.items()})
+    torch.cuda.synchronize()
+    ref = oracle.moe_forward(wl.x, r13, rs13, r2, rs2, 1, ids, w, I=I, **kw)
+    check_close_bf16_out(out_f64(out), ref, f"gemv-mfma int4 T={T} E={E} k={topk} H={H} I={I} bias={bias}")
+
+
 @pytest.mark.parametrize("T,H,I,E,topk,hot", [
     (256, 512, 512, 8, 4, 0),    # ~128 rows per expert: 4-block super-blocks
     (512, 768, 256, 4, 3, 0),    # ~384 rows per expert: two super-blocks each
