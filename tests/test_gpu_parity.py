@@ -883,10 +883,13 @@ def test_zero_tokens_is_noop(moe):
 # ------------------------------------------------------------- graph replay --
 
 @pytest.mark.parametrize("T,H,I,E,k,fused", [
-    (7, 512, 256, 16, 4, False),   # separate route and sort calls, wave-per-tile kernels
+    (7, 512, 256, 16, 4, False),   # separate route and sort calls, matrix-core GEMV kernels
     (1, 512, 1024, 16, 4, True),   # fused small routing, GEMV gate_up and down, combine
-    (8, 512, 256, 8, 4, True),     # single-wave MFMA tiles
-    (40, 512, 256, 8, 4, True),    # workgroup routing, 4-wave tiles with super-blocks
+    (1, 512, 256, 200, 8, True),   # one token over 200 experts: workgroup routing + align
+    (8, 512, 256, 8, 4, True),     # matrix-core GEMV kernels, two passes per full block
+    (14, 512, 256, 8, 4, True),    # activations shared by the workgroup
+    (20, 512, 256, 8, 4, True),    # 32-row blocks: single-wave and 4-wave MFMA tiles
+    (40, 512, 256, 8, 4, True),    # 4-wave tiles with super-blocks
 ])
 def test_graph_replay_matches_eager(moe, T, H, I, E, k, fused):
     """The whole layer captured in a HIP graph (no allocation or memset inside):
