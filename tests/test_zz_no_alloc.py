@@ -33,11 +33,14 @@ def _inputs(moe, wl, T, dev):
 
 def test_noalloc_matches_forward_two_calls(moe):
     dev = torch.device("cuda")
-    wl = synth.make(synth.specs()["decode_t16"])
+    wl = synth.make(synth.specs()["decode_t32"])
     s = wl.spec
     w13, w13s, w2, w2s = (torch.from_numpy(a).to(dev) for a in (wl.w13, wl.w13_scale, wl.w2, wl.w2_scale))
     cases = []
-    for T in (16, 3):  # 32-row MFMA tiles first, then the GEMV kernels on 16-row blocks
+    # 32-row MFMA tiles, then 16-row blocks on the matrix-core kernels (with
+    # the activations shared by the workgroup, then per wave): each call
+    # smaller than the one before.
+    for T in (32, 16, 3):
         x, ids, w, srt, be, npp, bm = _inputs(moe, wl, T, dev)
         ref = moe.moe_a16w4_forward(x, w13, w13s, w2, w2s, ids, w, srt, be, npp, bm)
         out = torch.empty((T, s.H), dtype=torch.bfloat16, device=dev)
