@@ -213,10 +213,15 @@ def fused_t1(T, fmt, H, I, topk, E):
 
 def stage1_kernel_name(T, bm, fmt, H, I, topk, E):
     """Which gate_up kernel the library launches for this shape (the rule of
-    gemv_mfma_eligible / gemv_eligible / forward_stages in the C sources, restated for the label)."""
+    gemv_resident_eligible / gemv_mfma_eligible / gemv_eligible / forward_stages
+    in the C sources, restated for the label)."""
     if fused_t1(T, fmt, H, I, topk, E):
         return "route_gate_up_t1_kernel"
     rows = min(T, bm)
+    cap16 = T * topk + min(T * topk, E) * 15  # align/sort capacity at 16-row blocks
+    if (bm == 16 and rows > 1 and fmt == 0 and H <= 4096 and I <= 4096 and H % 512 == 0 and I % 512 == 0
+            and (cap16 + 15) // 16 <= 512):
+        return "gemv_resident_kernel"
     if (bm == 16 and rows > 1 and H <= 4096 and I <= 4096 and H % 64 == 0 and I % 64 == 0):
         return "gemv_mfma_x_kernel" if T > 12 else "stage1_gemv_mfma_kernel"
     if (bm <= 32 and fmt == 0 and rows <= 8 and H <= 4096 and I <= 4096

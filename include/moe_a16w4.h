@@ -86,7 +86,7 @@ moe_status moe_route_topk(const float* logits, int T, int E, int topk, int renor
 int64_t moe_align_sort_capacity(int T, int topk, int E, int block_m);
 
 /* Block size the forward works best with for this token count
- * (16 up to 16 tokens, else 32). */
+ * (16 up to 48 tokens, else 32). */
 int moe_default_block_m(int T, int topk, int E);
 
 /* Group the P = T*topk (token, slot) pairs by expert for the grouped GEMMs

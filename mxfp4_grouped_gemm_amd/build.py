@@ -14,7 +14,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe_a16w4.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["abi.cpp", "route.hip", "route_t1.hip", "align_sort.hip", "gemm_stream.hip", "gemm_decode.hip", "gemm_gemv.hip", "gemv_mfma.hip", "gemm_prefill.hip", "gemm_prefill_int4.hip", "decode_t1.hip", "combine.hip", "requant.hip"]
+SOURCES = ["abi.cpp", "route.hip", "route_t1.hip", "align_sort.hip", "gemm_stream.hip", "gemm_decode.hip", "gemm_gemv.hip", "gemv_mfma.hip", "gemv_resident.hip", "gemm_prefill.hip", "gemm_prefill_int4.hip", "decode_t1.hip", "combine.hip", "requant.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",

@@ -220,12 +220,11 @@ int64_t moe_align_sort_capacity(int T, int topk, int E, int block_m) {
 int moe_default_block_m(int T, int topk, int E) {
     (void)topk;
     (void)E;
-    // 16-row blocks on the matrix-core GEMV kernels up to 16 tokens (gate_up
-    // at 12 tokens 191 against 218 us on the 32-row tiles, at 16 tokens 216
-    // against 233 with the block's activations shared by the workgroup);
-    // above, the 32-row tiles (32 tokens: 261 us either way, skewed 239
-    // against 285).
-    if (T <= 16) return 16;
+    // 16-row blocks on the matrix-core decode kernels up to 48 tokens (MXFP4
+    // gate_up with the block's rows resident in LDS: 190 against 233 us on
+    // the 32-row tiles at 16 tokens, 225 against 263 at 32, 255 against 266
+    // at 48, but 285 against 269 at 64); above, the 32-row tiles.
+    if (T <= 48) return 16;
     return 32;
 }
 

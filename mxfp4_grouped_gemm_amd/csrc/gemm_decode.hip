@@ -299,6 +299,7 @@ static hipError_t launch_decode_fmt(const MoeGemmArgs& a, int stage, hipStream_t
 
 hipError_t launch_decode_stage(const MoeGemmArgs& a, int stage, hipStream_t s) {
     const int rows = a.T < a.bm ? a.T : a.bm;
+    if (rows > 1 && gemv_resident_eligible(a)) return launch_gemv_resident_stage(a, stage, s);
     if (a.T > 12 && gemv_mfma_eligible(a)) return launch_gemv_mfma_x_stage(a, stage, s);
     if (rows > 1 && gemv_mfma_eligible(a)) return launch_gemv_mfma_stage(a, stage, s);
     if (gemv_eligible(a)) return launch_gemv_stage(a, stage, s);

@@ -98,6 +98,11 @@ hipError_t launch_gemv_mfma_stage(const MoeGemmArgs& a, int stage, hipStream_t s
 // The same with the block's activation rows staged once per workgroup in LDS
 // and up to 8 token rows per pass (blocks holding many rows).
 hipError_t launch_gemv_mfma_x_stage(const MoeGemmArgs& a, int stage, hipStream_t s);
+// The same products with the block's rows resident in LDS for a run of
+// units, one 8-wave workgroup per compute unit (MXFP4, H and I multiples of
+// 512 up to 4096).
+bool gemv_resident_eligible(const MoeGemmArgs& a);
+hipError_t launch_gemv_resident_stage(const MoeGemmArgs& a, int stage, hipStream_t s);
 
 // LDS-tiled MFMA kernels for prefill sizes (MXFP4, 32-row blocks, H and I
 // multiples of 256). Stage 1 first cuts the sorted blocks into super-blocks

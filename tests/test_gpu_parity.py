@@ -357,6 +357,37 @@ def test_forward_gemv_mfma_shared_x_blocks(moe, T, E, topk, H, I):
     check_close_bf16_out(out_f64(out), ref, f"gemv-mfma-x T={T} E={E} k={topk} H={H} I={I}")
 
 
+@pytest.mark.parametrize("T,E,topk,H,I,hot,bias", [
+    (2, 8, 4, 512, 512, 0, False),      # 1-2 rows per block: one token group
+    (7, 16, 6, 1024, 512, 0, False),    # up to 7 rows: one or two groups
+    (16, 8, 8, 512, 1024, 0, False),    # topk == E: every block 16 rows, four groups
+    (12, 6, 3, 1536, 1024, 0, False),   # K = 1536 / 1024: three and two 512-element chunks
+    (32, 4, 4, 512, 512, 0, False),     # two full 16-row blocks per expert
+    (24, 40, 20, 1024, 512, 0, False),  # topk above 16, many blocks
+    (20, 12, 3, 512, 1024, 3, False),   # skewed: hot experts' blocks full, the rest 1-3 rows
+    (5, 7, 7, 4096, 4096, 0, False),    # largest H and I: several units per wave, block changes inside a workgroup
+    (9, 8, 4, 512, 1024, 0, True),      # biases and the clamp
+])
+def test_forward_resident_blocks(moe, T, E, topk, H, I, hot, bias):
+    """16-row blocks with H and I multiples of 512 take the persistent
+    matrix-core kernels that keep the block's activation rows in LDS (one or
+    two or four token groups; weights of the next unit in flight across unit
+    and block changes); every token compared."""
+    wl = synth.small(T=T, H=H, I=I, E=E, topk=topk, seed=110 + T + H + I, hot=hot)
+    ids, w = oracle.route_topk(wl.logits, topk)
+    kw = {}
+    if bias:
+        b13, b2 = synth.biases(E, H, I, seed=T + E + 1)
+        kw = dict(w13_bias=b13, w2_bias=b2, swiglu_limit=100.0)
+    x = x_dev(wl)
+    w13, w13s, w2, w2s = weights_dev(wl)
+    out = moe.moe_a16w4_layer(x, dev(wl.logits), w13, w13s, w2, w2s, topk, block_m=16,
+                              **{k: (dev(v, torch.bfloat16) if k != "swiglu_limit" else v) for k, v in kw.items()})
+    torch.cuda.synchronize()
+    ref = oracle.moe_forward(wl.x, wl.w13, wl.w13_scale, wl.w2, wl.w2_scale, 0, ids, w, I=I, **kw)
+    check_close_bf16_out(out_f64(out), ref, f"resident T={T} E={E} k={topk} H={H} I={I} hot={hot} bias={bias}")
+
+
 @pytest.mark.parametrize("T,E,topk,H,I,bias", [
     (3, 8, 4, 512, 256, False),     # 2-4 rows: one token group, one pass
     (8, 4, 3, 640, 384, False),     # up to 8 rows: two passes; partial last chunk (K = 640)
@@ -478,6 +509,7 @@ BIAS_CASES = [
     (2, 512, 1024, 40, 20, None, 0, "bc"), # topk above 16: the combine's slot loop
     (16, 512, 256, 8, 4, 32, 0, "bc"),     # single-wave MFMA tiles (gate_up and down)
     (16, 512, 256, 8, 4, 16, 0, "bc"),     # 16-row blocks, activations shared by the workgroup
+    (12, 512, 512, 8, 4, 16, 0, "bc"),     # 16-row blocks, activations resident in LDS
     (24, 512, 256, 12, 3, 32, 1, "bc"),    # int4 single-wave tiles
     (256, 512, 512, 8, 4, None, 0, "bc"),  # 4-wave LDS tiles with super-blocks
     (96, 512, 256, 8, 4, None, 1, "bc"),   # int4 on the 4-wave tiles
