@@ -1,11 +1,12 @@
-// Decode GEMMs (MXFP4 weights, expert blocks of up to 16 token rows) with
-// the block's activation rows resident in LDS, in a persistent grid of one
-// 8-wave workgroup per compute unit.
+// Decode GEMMs (MXFP4 or int4-g32 weights, expert blocks of up to 16 token
+// rows) with the block's activation rows resident in LDS, in a persistent
+// grid of one 8-wave workgroup per compute unit.
 //
 // The products are those of gemv_mfma.hip (v_mfma_f32_4x4x4_16b_bf16, lane
-// 4 seg + r holding MX block seg of weight row r and the same K range of
-// token row r, 16 weight rows x up to 16 token rows per wave), but the
-// activation side no longer travels with every chunk of weights:
+// 4 seg + r holding MX block (int4: 32-group) seg of weight row r and the
+// same K range of token row r, 16 weight rows x up to 16 token rows per
+// wave), but the activation side no longer travels with every chunk of
+// weights:
 //  * the workgroup copies the rows of its current expert block (all of K,
 //    up to 16 rows: 115 KB at K = 3584) into LDS once, when its run of units
 //    enters the block, and every wave reads its MFMA operands from there;
@@ -16,26 +17,28 @@
 //    of 4 rows x 256 bytes per instruction) and loads the next unit's chunk
 //    c as soon as it has decoded chunk c of the current one, so one unit of
 //    weights (28 KB at K = 3584) is in flight per wave at all times, across
-//    unit and block boundaries.
-// The token groups of a block (4 rows each) select a specialisation of the
-// unit (1, 2 or 4 groups), so blocks of a few rows issue no MFMAs for the
-// empty ones. The per-unit scales and the row pairs come from LDS and the
-// stage-1 biases are loaded at the start of the unit, so the epilogue never
-// waits on global memory behind the next unit's weights.
+//    unit and block boundaries;
+//  * the runs are cut so that every workgroup gets the same summed cost: a
+//    unit costs more with more token groups, and with equal step counts the
+//    few workgroups holding the fullest blocks would finish last.
+// The token groups of a block (4 rows each) are multiplied behind uniform
+// branches, so blocks of a few rows issue no MFMAs for the empty ones. int4
+// weights take at most two groups per pass (the per-chunk group sums need
+// the registers of the other two): a block of more than 8 rows runs each
+// unit twice. The per-unit scales, the row pairs and (int4) the activation
+// sums of each row and 32-group come from LDS, and the stage-1 biases are
+// loaded at the start of the unit, so the epilogue never waits on global
+// memory behind the next unit's weights.
 // LDS rows have a stride of 2 K + 16 bytes and are filled 4 rows x 4 pieces
 // (64 bytes apart) per 16 lanes; with K a multiple of 512 both the fill and
 // the operand reads touch each of the 64 banks once per 16 lanes.
-#include <type_traits>
-
 #include "gemv_mfma.hpp"
 
 namespace moe {
 
 constexpr int kPxWaves = 8;   // waves per workgroup: two per SIMD
 constexpr int kPxRows = 16;   // token rows of a block held in LDS
-constexpr int kPxMaxK = 4096;
 constexpr int kPxMaxBlocks = kPxWaves * 64;  // expert blocks a launch may hold: one per thread
-constexpr uint32_t kPxSpare = kPxRows * (2 * kPxMaxK + 16);  // a 16-byte slot past the rows
 
 template <int NCH>
 struct PxRing {
@@ -50,11 +53,18 @@ struct PxUnit {
     rsrc_t rw, rs;  // the expert's weight codes and scales from row c0 on
 };
 
-template <int STAGE, int NCH, bool EPI>
+template <int FMT, int STAGE, int NCH, bool EPI>
 __global__ __launch_bounds__(kPxWaves * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void gemv_resident_kernel(MoeGemmArgs a) {
-    __shared__ __attribute__((aligned(16))) uint8_t xt[kPxRows * (2 * kPxMaxK + 16) + 16];
-    __shared__ __attribute__((aligned(16))) uint8_t lds_scale[kPxWaves][16 * kPxMaxK / 32];
+    constexpr bool kInt4 = FMT == kFmtInt4g32;
+    constexpr int K = 512 * NCH, nblk = K / 32;  // K = H (stage 1) or I (stage 2)
+    constexpr int SB = kInt4 ? 2 : 1;            // bytes per scale
+    constexpr int kPassG = kInt4 ? 2 : 4;        // token groups per pass
+    constexpr uint32_t xstride = 2u * K + 16u;
+    constexpr uint32_t kSpare = kPxRows * xstride;  // a 16-byte slot past the rows
+    __shared__ __attribute__((aligned(16))) uint8_t xt[kSpare + 16];
+    __shared__ __attribute__((aligned(16))) uint8_t lds_scale[kPxWaves][16 * nblk * SB];
+    __shared__ float xsum[kInt4 ? kPxRows * nblk : 1];  // int4: sum of each row's 32-groups
     __shared__ uint32_t rowoff[kPxRows];
     __shared__ int32_t rowpair[kPxRows];
     __shared__ uint32_t wsum[kPxWaves];
@@ -62,23 +72,19 @@ void gemv_resident_kernel(MoeGemmArgs a) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int H = a.H, I = a.I;
-    constexpr int K = 512 * NCH, nblk = K / 32;  // K = H (stage 1) or I (stage 2)
-    constexpr uint32_t xstride = 2u * K + 16u;
-    const int upb = STAGE == 1 ? I / 8 : H / 16;      // units per block
-    const int spb = upb / kPxWaves;                   // steps per block
+    const int upb = STAGE == 1 ? I / 8 : H / 16;  // units per block
+    const int spb = upb / kPxWaves;               // steps per block
     const int P = a.T * a.topk;
     int64_t nused = *a.num_post_pad / a.bm;
     if (nused > a.cap / a.bm) nused = a.cap / a.bm;  // at most kPxMaxBlocks (launcher)
     const int64_t S = nused * spb;
     if (S == 0) return;
 
-    // Cost-balanced runs of steps. A unit costs more with more token groups
-    // (measured per unit with every block at 1, 2 or 4 groups: 1 : 1.07 :
-    // 1.46), so the workgroups split the blocks' summed cost evenly rather
-    // than the step count; otherwise the few workgroups that hold the
-    // fullest blocks finish last. Thread b weighs block b (its pairs counted
-    // from the sort), a workgroup scan gives the prefix, and the block that
-    // holds each of this workgroup's two cut points places it.
+    // Cost-balanced runs of steps: thread b weighs block b by its rows (the
+    // pairs in the sort; measured per unit with every block at 1, 2 or 4
+    // groups, 1 : 1.07 : 1.46 for MXFP4; int4 runs 4 groups as two passes of
+    // 2), a workgroup scan gives the prefix, and the block that holds each of
+    // this workgroup's two cut points places it.
     {
         const rsrc_t rsid = make_rsrc(a.sorted_ids, (uint32_t)(a.cap * 4));
         const bool mine = tid < nused;
@@ -89,7 +95,7 @@ void gemv_resident_kernel(MoeGemmArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) cnt += ((int)v[i] >= 0 && (int)v[i] < P) ? 1 : 0;
         }
-        const uint32_t cost = mine ? (cnt > 8 ? 19u : cnt > 4 ? 14u : 13u) : 0u;
+        const uint32_t cost = !mine ? 0u : cnt > 8 ? (kInt4 ? 28u : 19u) : cnt > 4 ? 14u : 13u;
         uint32_t incl = cost;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
@@ -124,10 +130,10 @@ void gemv_resident_kernel(MoeGemmArgs a) {
     const rsrc_t rx = STAGE == 1 ? make_rsrc(a.x, (uint32_t)((int64_t)a.T * H * 2))
                                  : make_rsrc(a.h, (uint32_t)((int64_t)P * I * 2));
     uint8_t* lds = lds_scale[wave];
-    // This lane's scale bytes in the wave's LDS rows (runs staged in order):
-    // row (stage 1) r < 2 ? r + 2s : r + 6 + 2s, (stage 2) r + 4s; byte seg of
-    // each chunk's 16.
-    const uint8_t* lsc = lds + (STAGE == 1 ? (r < 2 ? r : r + 6) : r) * nblk + seg;
+    // This lane's scales in the wave's LDS rows (runs staged in order): row
+    // (stage 1) r < 2 ? r + 2s : r + 6 + 2s, (stage 2) r + 4s; element seg
+    // of each chunk's 16.
+    const int lsc = (STAGE == 1 ? (r < 2 ? r : r + 6) : r) * nblk + seg;
     constexpr int kScSetStride = (STAGE == 1 ? 2 : 4) * nblk;
 
     // The experts of the workgroup's blocks (at most 64), one per lane, loaded
@@ -145,25 +151,24 @@ void gemv_resident_kernel(MoeGemmArgs a) {
         const int64_t row = (ok ? u.e : 0) * slab_rows + u.c0;
         const uint32_t rows_left = ok ? (uint32_t)(slab_rows - u.c0) : 0u;
         u.rw = make_rsrc(wbase + row * (K / 2), rows_left * (K / 2));
-        u.rs = make_rsrc(sbase + row * nblk, rows_left * nblk);
+        u.rs = make_rsrc(sbase + row * nblk * SB, rows_left * nblk * SB);
     };
-    // Lane offsets from row c0 of the unit: this lane's row of set s (stage 1:
-    // gate c0 + 2s + r or up I + c0 + 2s + r - 2; stage 2: c0 + 4s + r),
-    // segment seg; and its 16-byte pieces of the unit's scale rows (stage 1:
-    // the gate run, then the up run I rows on).
-    // Set s adds a whole number of rows (2 s in stage 1, 4 s in stage 2),
-    // which goes into the scalar offset of the load.
+    // Lane offset from row c0 of the unit: this lane's row of set 0 (stage
+    // 1: gate c0 + r or up I + c0 + r - 2; stage 2: c0 + r), segment seg. Set
+    // s adds a whole number of rows (2 s in stage 1, 4 s in stage 2), which
+    // goes into the scalar offset of the load.
     const uint32_t woff = (uint32_t)(STAGE == 1 ? (r < 2 ? r : I + r - 2) : r) * (uint32_t)(K / 2) + 16u * seg;
     constexpr uint32_t kSetStride = (STAGE == 1 ? 2 : 4) * (K / 2);
-    // The unit's 16 rows of scale bytes (nblk each, two runs in stage 1) as
-    // 16-byte pieces: two per lane at most (nblk <= 128).
-    auto issue_scales = [&](const PxUnit<STAGE>& u, u32x4 (&sc)[2]) {
+    // The unit's 16 rows of scales (nblk each, two runs in stage 1) as
+    // 16-byte pieces: kScPieces per lane.
+    constexpr int kScPieces = (nblk * SB + 63) / 64;
+    auto issue_scales = [&](const PxUnit<STAGE>& u, u32x4 (&sc)[kScPieces], uint32_t mask) {
 #pragma unroll
-        for (int k = 0; k < 2; ++k) {
+        for (int k = 0; k < kScPieces; ++k) {
             const int p = lane + 64 * k;
-            constexpr int p0 = (STAGE == 1 ? 8 : 16) * nblk / 16;
-            const uint32_t so = p < p0 ? 16u * p : p < nblk ? (uint32_t)I * nblk + 16u * (p - p0) : kOob;
-            sc[k] = bld16nt(u.rs, so);
+            constexpr int p0 = (STAGE == 1 ? 8 : 16) * nblk * SB / 16;
+            const uint32_t so = p < p0 ? 16u * p : p < nblk * SB ? (uint32_t)I * nblk * SB + 16u * (p - p0) : kOob;
+            sc[k] = bld16nt(u.rs, so | mask);
             __builtin_amdgcn_sched_barrier(0);
         }
     };
@@ -178,7 +183,9 @@ void gemv_resident_kernel(MoeGemmArgs a) {
         }
     };
 
-    // The block's rows into LDS; returns its token groups (1..4).
+    // The block's rows into LDS (int4: each 16-byte piece in the codes'
+    // element order, and the sums of each row's 32-groups); returns its
+    // token groups (1, 2 or 4).
     auto fill_x = [&](int64_t b) -> int {
         const int64_t row0 = b * a.bm;
         const int p = a.sorted_ids[row0 + (lane & 15)];
@@ -196,8 +203,9 @@ void gemv_resident_kernel(MoeGemmArgs a) {
         // free: elements past the end load nothing (kOob) and are stored to a
         // spare slot, so every load is consumed on the one path (a load left
         // pending on some path would make later waits conservative).
-        const int mper = K / 128;  // pieces per row / 16
+        constexpr int mper = K / 128;  // pieces per row / 16
         const int total = 64 * ng * mper;
+#pragma unroll 1
         for (int base = 0; base < total; base += kPxWaves * 64 * 2) {
             u32x4 v[2];
             uint32_t dst[2];
@@ -209,74 +217,140 @@ void gemv_resident_kernel(MoeGemmArgs a) {
                 const int row = (4 * rq + rl) & (kPxRows - 1), piece = 16 * m + 4 * pj + n;
                 const uint32_t ro = i < total ? rowoff[row] : kOob;
                 v[j] = bld16(rx, ro + 16u * piece);  // kOob + 16 piece stays past the record
-                dst[j] = i < total ? (uint32_t)row * xstride + 16u * piece : kPxSpare;
+                if constexpr (kInt4) v[j] = __builtin_bit_cast(u32x4, perm_x_int4(__builtin_bit_cast(bf16x8, v[j])));
+                dst[j] = i < total ? (uint32_t)row * xstride + 16u * piece : kSpare;
             }
 #pragma unroll
             for (int j = 0; j < 2; ++j) *(u32x4*)(xt + dst[j]) = v[j];
         }
         __syncthreads();
+        if constexpr (kInt4) {
+            // Sum of each (row, 32-group): four 16-byte pieces, fp32, in order.
+#pragma unroll 1
+            for (int i = tid; i < 4 * ng * nblk; i += kPxWaves * 64) {
+                const int row = i / nblk, grp = i - row * nblk;
+                const uint8_t* src = xt + (uint32_t)row * xstride + 64u * grp;
+                float sum = 0.0f;
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    const u32x4 v = *(const u32x4*)(src + 16 * k);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) sum += __uint_as_float(v[e] << 16) + __uint_as_float(v[e] & 0xffff0000u);
+                }
+                xsum[i] = sum;
+            }
+            __syncthreads();
+        }
         return ng;
     };
 
-    // Chunk c of a unit against the block's ng token groups: the decode and
-    // group 0 on every path, groups 1 and 2-3 behind uniform branches per K
-    // step (whole-chunk bodies per group count let the compiler hoist the
-    // shared decode of all four steps above the branch).
-    auto consume = [&](int ng, const u32x4 (&w)[kGmSets], int c, f32x4 (&acc)[4][kGmSets]) {
+    // Chunk c of a unit against token groups g0 .. g0 + ngp - 1 (acc[g - g0]):
+    // the decode and the first group on every path, the others behind uniform
+    // branches (whole-chunk bodies per group count let the compiler hoist the
+    // shared decode of all four K steps above the branch).
+    auto consume = [&](int g0, int ngp, const u32x4 (&w)[kGmSets], int c, f32x4 (&acc)[kPassG][kGmSets]) {
         const int blk = 16 * c + seg;
-        float sc[kGmSets];
+        if constexpr (!kInt4) {
+            float sc[kGmSets];
 #pragma unroll
-        for (int s = 0; s < kGmSets; ++s) sc[s] = e8m0_scale_operand(lsc[kScSetStride * s + 16 * c]);
-        auto group = [&](const bf16x8 (&wv)[kGmSets], int g, int q) {
-            const bf16x8 xv = *(const bf16x8*)(xt + (uint32_t)(4 * g + r) * xstride + 64u * blk + 16u * q);
+            for (int s = 0; s < kGmSets; ++s) sc[s] = e8m0_scale_operand(lds[lsc + kScSetStride * s + 16 * c]);
+            auto group = [&](const bf16x8 (&wv)[kGmSets], int gi, int q) {
+                const bf16x8 xv = *(const bf16x8*)(xt + (uint32_t)(4 * (g0 + gi) + r) * xstride + 64u * blk + 16u * q);
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const bf16x4_t xh = h ? __builtin_shufflevector(xv, xv, 4, 5, 6, 7)
-                                      : __builtin_shufflevector(xv, xv, 0, 1, 2, 3);
+                for (int h = 0; h < 2; ++h) {
+                    const bf16x4_t xh = h ? __builtin_shufflevector(xv, xv, 4, 5, 6, 7)
+                                          : __builtin_shufflevector(xv, xv, 0, 1, 2, 3);
 #pragma unroll
-                for (int s = 0; s < kGmSets; ++s) {
-                    const bf16x4_t wb = h ? __builtin_shufflevector(wv[s], wv[s], 4, 5, 6, 7)
-                                          : __builtin_shufflevector(wv[s], wv[s], 0, 1, 2, 3);
-                    acc[g][s] = mfma4x4(wb, xh, acc[g][s]);
+                    for (int s = 0; s < kGmSets; ++s) {
+                        const bf16x4_t wb = h ? __builtin_shufflevector(wv[s], wv[s], 4, 5, 6, 7)
+                                              : __builtin_shufflevector(wv[s], wv[s], 0, 1, 2, 3);
+                        acc[gi][s] = mfma4x4(wb, xh, acc[gi][s]);
+                    }
+                }
+            };
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                bf16x8 wv[kGmSets];
+#pragma unroll
+                for (int s = 0; s < kGmSets; ++s) wv[s] = mxfp4x8_to_bf16(w[s][q], sc[s]);
+                group(wv, 0, q);
+                if (ngp > 1) group(wv, 1, q);
+                if (ngp > 2) {
+                    group(wv, 2, q);
+                    group(wv, 3, q);
                 }
             }
-        };
+        } else {
+            // Per group: the products of code + 136 with the permuted
+            // activations over the lane's 32-group, then the fold with the
+            // group's bf16 scale and activation sum (gm_int4_fold).
+            const uint16_t* lsc16 = (const uint16_t*)lds + lsc + 16 * c;
+            float sc[kGmSets];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            bf16x8 wv[kGmSets];
+            for (int s = 0; s < kGmSets; ++s) sc[s] = bf16_bits_to_f32(lsc16[kScSetStride * s]);
+            // K steps outer (the decode shared by the groups), groups inner.
+            f32x4 t[kPassG][kGmSets];
 #pragma unroll
-            for (int s = 0; s < kGmSets; ++s) wv[s] = mxfp4x8_to_bf16(w[s][q], sc[s]);
-            group(wv, 0, q);
-            if (ng > 1) group(wv, 1, q);
-            if (ng > 2) {
-                group(wv, 2, q);
-                group(wv, 3, q);
+            for (int gi = 0; gi < kPassG; ++gi)
+#pragma unroll
+                for (int s = 0; s < kGmSets; ++s) t[gi][s] = f32x4{0.f, 0.f, 0.f, 0.f};
+            auto group = [&](const bf16x8 (&wv)[kGmSets], int gi, int q) {
+                const bf16x8 xv = *(const bf16x8*)(xt + (uint32_t)(4 * (g0 + gi) + r) * xstride + 64u * blk + 16u * q);
+                const bf16x4_t x0 = __builtin_shufflevector(xv, xv, 0, 1, 2, 3);
+                const bf16x4_t x1 = __builtin_shufflevector(xv, xv, 4, 5, 6, 7);
+#pragma unroll
+                for (int s = 0; s < kGmSets; ++s) {
+                    t[gi][s] = mfma4x4(__builtin_shufflevector(wv[s], wv[s], 0, 1, 2, 3), x0, t[gi][s]);
+                    t[gi][s] = mfma4x4(__builtin_shufflevector(wv[s], wv[s], 4, 5, 6, 7), x1, t[gi][s]);
+                }
+            };
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                bf16x8 wv[kGmSets];
+#pragma unroll
+                for (int s = 0; s < kGmSets; ++s) wv[s] = int4x8_to_bf16_biased(w[s][q]);
+                group(wv, 0, q);
+                if (ngp > 1) group(wv, 1, q);
             }
+            auto fold = [&](int gi) {
+                const float xs1 = xsum[(4 * (g0 + gi) + r) * nblk + blk];  // token r of the group
+                const f32x4 xs = {xs1, xs1, xs1, xs1};
+#pragma unroll
+                for (int s = 0; s < kGmSets; ++s) gm_int4_fold(t[gi][s], xs, sc[s], acc[gi][s]);
+            };
+            fold(0);
+            if (ngp > 1) fold(1);
+            // Each chunk's fold stays in its chunk (the compiler would sink
+            // them all to the unit's end, keeping every chunk's products live).
+#pragma unroll
+            for (int gi = 0; gi < kPassG; ++gi)
+#pragma unroll
+                for (int s = 0; s < kGmSets; ++s) asm volatile("" : "+v"(acc[gi][s]));
         }
     };
-    // One unit: consumes the ring and refills it with the next unit's chunks
-    // (mask: kOob when there is none). The refill is on the one common path,
-    // so the loads in flight keep their registers across units (per-unit
-    // bodies that each reloaded the ring were joined by register copies,
-    // which wait for every load).
-    auto run_unit = [&](int ng, PxRing<NCH>& ring, const PxUnit<STAGE>& cur, const PxUnit<STAGE>& nxt,
+    // One unit (one pass): consumes the ring and refills it with the next
+    // unit's chunks (mask: kOob when there is none). The refill is on the one
+    // common path, so the loads in flight keep their registers across units
+    // (per-unit bodies that each reloaded the ring were joined by register
+    // copies, which wait for every load).
+    auto run_unit = [&](int g0, int ngp, PxRing<NCH>& ring, const PxUnit<STAGE>& cur, const PxUnit<STAGE>& nxt,
                         uint32_t mask, uint32_t bg, uint32_t bu) {
-        f32x4 acc[4][kGmSets];
+        f32x4 acc[kPassG][kGmSets];
 #pragma unroll
-        for (int g = 0; g < 4; ++g)
+        for (int g = 0; g < kPassG; ++g)
 #pragma unroll
             for (int s = 0; s < kGmSets; ++s) acc[g][s] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
-            consume(ng, ring.w[c], c, acc);
+            consume(g0, ngp, ring.w[c], c, acc);
             issue_chunk(ring, nxt, c, mask);
             __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            if (g >= ng) break;
-            gm_reduce(acc[g]);
-            const int pr = rowpair[4 * g + r];
+        for (int gi = 0; gi < kPassG; ++gi) {
+            if (gi >= ngp) break;
+            gm_reduce(acc[gi]);
+            const int pr = rowpair[4 * (g0 + gi) + r];
             if constexpr (STAGE == 1) {
                 // Lane 4c + j with c < 8 stores (token j, column c0 + 2 (c & 3) + (c >> 2)).
                 const int sel = seg & 3, half = (seg >> 2) & 1;
@@ -284,8 +358,8 @@ void gemv_resident_kernel(MoeGemmArgs a) {
                 float gv = 0.f, uv = 0.f;
 #pragma unroll
                 for (int s = 0; s < kGmSets; ++s) {
-                    gv = s == sel ? (half ? acc[g][s][1] : acc[g][s][0]) : gv;
-                    uv = s == sel ? (half ? acc[g][s][3] : acc[g][s][2]) : uv;
+                    gv = s == sel ? (half ? acc[gi][s][1] : acc[gi][s][0]) : gv;
+                    uv = s == sel ? (half ? acc[gi][s][3] : acc[gi][s][2]) : uv;
                 }
                 if (lane < 32 && pr >= 0) {
                     if constexpr (EPI) {
@@ -306,7 +380,7 @@ void gemv_resident_kernel(MoeGemmArgs a) {
 #pragma unroll
                 for (int s = 0; s < kGmSets; ++s)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) v = (s == sel && i == slot) ? acc[g][s][i] : v;
+                    for (int i = 0; i < 4; ++i) v = (s == sel && i == slot) ? acc[gi][s][i] : v;
                 if (pr >= 0) a.y[(int64_t)pr * H + cur.c0 + 4 * sel + slot] = v;
             }
         }
@@ -314,15 +388,15 @@ void gemv_resident_kernel(MoeGemmArgs a) {
 
     PxUnit<STAGE> cur, nxt;
     unit_of(s0, cur);
-    u32x4 scn[2];
-    issue_scales(cur, scn);
+    u32x4 scn[kScPieces];
+    issue_scales(cur, scn, 0u);
     PxRing<NCH> ring;
 #pragma unroll
     for (int c = 0; c < NCH; ++c) issue_chunk(ring, cur, c, 0u);
     __builtin_amdgcn_sched_barrier(0);
     int64_t cb = -1;
-    int ng = 1;
-    for (int64_t s = s0; s < s1; ++s) {
+    int ng = 1, pass = 0;
+    for (int64_t s = s0; s < s1;) {
         if (cur.b != cb) {  // uniform: the workgroup's waves change block together
             ng = fill_x(cur.b);
             cb = cur.b;
@@ -330,8 +404,8 @@ void gemv_resident_kernel(MoeGemmArgs a) {
         // This unit's scales (loaded one unit ahead) into the wave's LDS rows;
         // the previous unit's reads of them are complete (LDS runs in order).
 #pragma unroll
-        for (int k = 0; k < 2; ++k)
-            if (lane + 64 * k < nblk) *(u32x4*)(lds + 16 * (lane + 64 * k)) = scn[k];
+        for (int k = 0; k < kScPieces; ++k)
+            if (lane + 64 * k < nblk * SB) *(u32x4*)(lds + 16 * (lane + 64 * k)) = scn[k];
         wave_lds_sync();
         // Stage-1 biases of this lane's output column, loaded ahead of the
         // next unit's weights; branch-free (no bias: an empty record reads
@@ -344,15 +418,22 @@ void gemv_resident_kernel(MoeGemmArgs a) {
             bg = __builtin_amdgcn_raw_buffer_load_b16(rb, 2u * col, 0, 0);
             bu = __builtin_amdgcn_raw_buffer_load_b16(rb, 2u * (I + col), 0, 0);
         }
-        const bool more = s + 1 < s1;
-        if (more) {
-            unit_of(s + 1, nxt);
-            issue_scales(nxt, scn);
-        } else {
-            nxt = cur;
-        }
+        // The next unit: this one again for its second pass (int4, blocks of
+        // more than 8 rows), else the next step's; none after the last.
+        const int g0 = kPassG * pass;
+        const int ngp = ng - g0 < kPassG ? ng - g0 : kPassG;
+        const bool again = g0 + kPassG < ng;
+        const bool more = again || s + 1 < s1;
+        unit_of(again ? s : s + 1, nxt);
         const uint32_t mask = more ? 0u : kOob;
-        run_unit(ng, ring, cur, nxt, mask, bg, bu);
+        issue_scales(nxt, scn, mask);
+        run_unit(g0, ngp, ring, cur, nxt, mask, bg, bu);
+        if (again) {
+            ++pass;
+        } else {
+            pass = 0;
+            ++s;
+        }
         cur = nxt;
     }
 }
@@ -371,22 +452,33 @@ static int resident_grid() {
 }
 
 // Every block is weighed by one thread, and a workgroup's run of steps
-// spans a few blocks (the kernel reads the experts of up to 64).
+// spans a few blocks (the kernel reads the experts of up to 64). K up to
+// 4096 (MXFP4) or 3584 (int4, whose scale rows take twice the LDS).
 bool gemv_resident_eligible(const MoeGemmArgs& a) {
-    return a.cap / 16 <= kPxMaxBlocks && resident_grid() >= 32 && a.fmt == kFmtMxfp4 && a.bm == 16 && a.H <= kPxMaxK && a.I <= kPxMaxK && a.H % 512 == 0 &&
-           a.I % 512 == 0 && (int64_t)a.T * a.topk * a.I * 2 < 0x7fff0000LL && (int64_t)a.T * a.H * 2 < 0x7fff0000LL;
+    const int kmax = a.fmt == kFmtMxfp4 ? 4096 : 3584;
+    return (a.fmt == kFmtMxfp4 || a.fmt == kFmtInt4g32) && a.bm == 16 && a.cap / 16 <= kPxMaxBlocks &&
+           resident_grid() >= 32 && a.H <= kmax && a.I <= kmax && a.H % 512 == 0 && a.I % 512 == 0 &&
+           (int64_t)a.T * a.topk * a.I * 2 < 0x7fff0000LL && (int64_t)a.T * a.H * 2 < 0x7fff0000LL;
+}
+
+template <int FMT, int NCH>
+static void launch_px_nch(const MoeGemmArgs& a, int stage, dim3 grid, dim3 block, hipStream_t s) {
+    if constexpr (FMT == kFmtInt4g32 && NCH > 7) {
+        return;  // not eligible
+    } else if (stage == 1) {
+        if (a.w13_bias || a.swiglu_limit > 0.0f)
+            hipLaunchKernelGGL((gemv_resident_kernel<FMT, 1, NCH, true>), grid, block, 0, s, a);
+        else
+            hipLaunchKernelGGL((gemv_resident_kernel<FMT, 1, NCH, false>), grid, block, 0, s, a);
+    } else {
+        hipLaunchKernelGGL((gemv_resident_kernel<FMT, 2, NCH, false>), grid, block, 0, s, a);
+    }
 }
 
 template <int NCH>
 static void launch_px_nch(const MoeGemmArgs& a, int stage, dim3 grid, dim3 block, hipStream_t s) {
-    if (stage == 1) {
-        if (a.w13_bias || a.swiglu_limit > 0.0f)
-            hipLaunchKernelGGL((gemv_resident_kernel<1, NCH, true>), grid, block, 0, s, a);
-        else
-            hipLaunchKernelGGL((gemv_resident_kernel<1, NCH, false>), grid, block, 0, s, a);
-    } else {
-        hipLaunchKernelGGL((gemv_resident_kernel<2, NCH, false>), grid, block, 0, s, a);
-    }
+    if (a.fmt == kFmtMxfp4) launch_px_nch<kFmtMxfp4, NCH>(a, stage, grid, block, s);
+    else launch_px_nch<kFmtInt4g32, NCH>(a, stage, grid, block, s);
 }
 
 hipError_t launch_gemv_resident_stage(const MoeGemmArgs& a, int stage, hipStream_t s) {

@@ -357,35 +357,47 @@ def test_forward_gemv_mfma_shared_x_blocks(moe, T, E, topk, H, I):
     check_close_bf16_out(out_f64(out), ref, f"gemv-mfma-x T={T} E={E} k={topk} H={H} I={I}")
 
 
-@pytest.mark.parametrize("T,E,topk,H,I,hot,bias", [
-    (2, 8, 4, 512, 512, 0, False),      # 1-2 rows per block: one token group
-    (7, 16, 6, 1024, 512, 0, False),    # up to 7 rows: one or two groups
-    (16, 8, 8, 512, 1024, 0, False),    # topk == E: every block 16 rows, four groups
-    (12, 6, 3, 1536, 1024, 0, False),   # K = 1536 / 1024: three and two 512-element chunks
-    (32, 4, 4, 512, 512, 0, False),     # two full 16-row blocks per expert
-    (24, 40, 20, 1024, 512, 0, False),  # topk above 16, many blocks
-    (20, 12, 3, 512, 1024, 3, False),   # skewed: hot experts' blocks full, the rest 1-3 rows
-    (5, 7, 7, 4096, 4096, 0, False),    # largest H and I: several units per wave, block changes inside a workgroup
-    (9, 8, 4, 512, 1024, 0, True),      # biases and the clamp
+@pytest.mark.parametrize("T,E,topk,H,I,hot,bias,fmt", [
+    (2, 8, 4, 512, 512, 0, False, 0),      # 1-2 rows per block: one token group
+    (7, 16, 6, 1024, 512, 0, False, 0),    # up to 7 rows: one or two groups
+    (16, 8, 8, 512, 1024, 0, False, 0),    # topk == E: every block 16 rows, four groups
+    (12, 6, 3, 1536, 1024, 0, False, 0),   # K = 1536 / 1024: three and two 512-element chunks
+    (32, 4, 4, 512, 512, 0, False, 0),     # two full 16-row blocks per expert
+    (24, 40, 20, 1024, 512, 0, False, 0),  # topk above 16, many blocks
+    (20, 12, 3, 512, 1024, 3, False, 0),   # skewed: hot experts' blocks full, the rest 1-3 rows
+    (5, 7, 7, 4096, 4096, 0, False, 0),    # largest H and I: several units per wave, block changes inside a workgroup
+    (9, 8, 4, 512, 1024, 0, True, 0),      # biases and the clamp
+    (5, 8, 4, 512, 512, 0, False, 1),      # int4-g32: one or two groups, one pass
+    (16, 8, 8, 512, 1024, 0, False, 1),    # int4, 16-row blocks: two passes of two groups per unit
+    (20, 12, 3, 1536, 1024, 3, True, 1),   # int4, skewed, biases and the clamp
+    (6, 5, 3, 3584, 3584, 0, False, 1),    # int4 at the largest K it takes (seven chunks)
 ])
-def test_forward_resident_blocks(moe, T, E, topk, H, I, hot, bias):
+def test_forward_resident_blocks(moe, T, E, topk, H, I, hot, bias, fmt):
     """16-row blocks with H and I multiples of 512 take the persistent
-    matrix-core kernels that keep the block's activation rows in LDS (one or
-    two or four token groups; weights of the next unit in flight across unit
-    and block changes); every token compared."""
-    wl = synth.small(T=T, H=H, I=I, E=E, topk=topk, seed=110 + T + H + I, hot=hot)
+    matrix-core kernels that keep the block's activation rows in LDS (one,
+    two or four token groups; int4 at most two per pass; weights of the next
+    unit in flight across unit and block changes); every token compared."""
+    wl = synth.small(T=T, H=H, I=I, E=E, topk=topk, seed=110 + T + H + I + fmt, hot=hot)
     ids, w = oracle.route_topk(wl.logits, topk)
     kw = {}
     if bias:
         b13, b2 = synth.biases(E, H, I, seed=T + E + 1)
         kw = dict(w13_bias=b13, w2_bias=b2, swiglu_limit=100.0)
-    x = x_dev(wl)
-    w13, w13s, w2, w2s = weights_dev(wl)
-    out = moe.moe_a16w4_layer(x, dev(wl.logits), w13, w13s, w2, w2s, topk, block_m=16,
+    if fmt == 0:
+        wts = weights_dev(wl)
+        r13, rs13, r2, rs2 = wl.w13, wl.w13_scale, wl.w2, wl.w2_scale
+    else:
+        q13, s13 = moe.requantize_mxfp4_experts(dev(wl.w13), dev(wl.w13_scale))
+        q2, s2 = moe.requantize_mxfp4_experts(dev(wl.w2), dev(wl.w2_scale))
+        wts = (q13, s13, q2, s2)
+        r13, rs13 = oracle.requant_int4g32(wl.w13, wl.w13_scale)
+        r2, rs2 = oracle.requant_int4g32(wl.w2, wl.w2_scale)
+    out = moe.moe_a16w4_layer(x_dev(wl), dev(wl.logits), *wts, topk, fmt=fmt, block_m=16,
                               **{k: (dev(v, torch.bfloat16) if k != "swiglu_limit" else v) for k, v in kw.items()})
     torch.cuda.synchronize()
-    ref = oracle.moe_forward(wl.x, wl.w13, wl.w13_scale, wl.w2, wl.w2_scale, 0, ids, w, I=I, **kw)
-    check_close_bf16_out(out_f64(out), ref, f"resident T={T} E={E} k={topk} H={H} I={I} hot={hot} bias={bias}")
+    ref = oracle.moe_forward(wl.x, r13, rs13, r2, rs2, fmt, ids, w, I=I, **kw)
+    check_close_bf16_out(out_f64(out), ref,
+                         f"resident T={T} E={E} k={topk} H={H} I={I} hot={hot} bias={bias} fmt={fmt}")
 
 
 @pytest.mark.parametrize("T,E,topk,H,I,bias", [
