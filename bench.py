@@ -219,7 +219,8 @@ def stage1_kernel_name(T, bm, fmt, H, I, topk, E):
         return "route_gate_up_t1_kernel"
     rows = min(T, bm)
     cap16 = T * topk + min(T * topk, E) * 15  # align/sort capacity at 16-row blocks
-    if (bm == 16 and rows > 1 and fmt == 0 and H <= 4096 and I <= 4096 and H % 512 == 0 and I % 512 == 0
+    kmax = 4096 if fmt == 0 else 3584
+    if (bm == 16 and rows > 1 and H <= kmax and I <= kmax and H % 512 == 0 and I % 512 == 0
             and (cap16 + 15) // 16 <= 512):
         return "gemv_resident_kernel"
     if (bm == 16 and rows > 1 and H <= 4096 and I <= 4096 and H % 64 == 0 and I % 64 == 0):
