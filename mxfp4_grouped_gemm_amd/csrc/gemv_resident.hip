@@ -68,6 +68,7 @@ void gemv_resident_kernel(MoeGemmArgs a) {
     __shared__ uint32_t rowoff[kPxRows];
     __shared__ int32_t rowpair[kPxRows];
     __shared__ uint32_t wsum[kPxWaves];
+    __shared__ int32_t bexp_lds[kPxMaxBlocks];
     __shared__ int64_t bound[2];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -75,8 +76,16 @@ void gemv_resident_kernel(MoeGemmArgs a) {
     const int upb = STAGE == 1 ? I / 8 : H / 16;  // units per block
     const int spb = upb / kPxWaves;               // steps per block
     const int P = a.T * a.topk;
+    // Everything the partition needs in one round trip: the block count,
+    // every block's sorted ids and its expert (thread b holds block b).
+    const int nbcap = (int)(a.cap / a.bm);  // at most kPxMaxBlocks (launcher)
+    const rsrc_t rsid = make_rsrc(a.sorted_ids, (uint32_t)(a.cap * 4));
+    u32x4 sid[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) sid[k] = bld16(rsid, tid < nbcap ? (uint32_t)tid * 64u + 16u * k : kOob);
+    const int bexp_t = tid < nbcap ? a.block_expert[tid] : -1;
     int64_t nused = *a.num_post_pad / a.bm;
-    if (nused > a.cap / a.bm) nused = a.cap / a.bm;  // at most kPxMaxBlocks (launcher)
+    if (nused > nbcap) nused = nbcap;
     const int64_t S = nused * spb;
     if (S == 0) return;
 
@@ -86,15 +95,13 @@ void gemv_resident_kernel(MoeGemmArgs a) {
     // 2), a workgroup scan gives the prefix, and the block that holds each of
     // this workgroup's two cut points places it.
     {
-        const rsrc_t rsid = make_rsrc(a.sorted_ids, (uint32_t)(a.cap * 4));
         const bool mine = tid < nused;
         int cnt = 0;
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const u32x4 v = bld16(rsid, mine ? (uint32_t)tid * 64u + 16u * k : kOob);
+        for (int k = 0; k < 4; ++k)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) cnt += ((int)v[i] >= 0 && (int)v[i] < P) ? 1 : 0;
-        }
+            for (int i = 0; i < 4; ++i) cnt += ((int)sid[k][i] >= 0 && (int)sid[k][i] < P) ? 1 : 0;
+        bexp_lds[tid] = bexp_t;
         const uint32_t cost = !mine ? 0u : cnt > 8 ? (kInt4 ? 28u : 19u) : cnt > 4 ? 14u : 13u;
         uint32_t incl = cost;
 #pragma unroll
@@ -136,11 +143,11 @@ void gemv_resident_kernel(MoeGemmArgs a) {
     const int lsc = (STAGE == 1 ? (r < 2 ? r : r + 6) : r) * nblk + seg;
     constexpr int kScSetStride = (STAGE == 1 ? 2 : 4) * nblk;
 
-    // The experts of the workgroup's blocks (at most 64), one per lane, loaded
-    // once: a unit's expert is a lane read (a vector load per unit would be
-    // waited for behind the weights already in flight).
+    // The experts of the workgroup's blocks (at most 64), one per lane: a
+    // unit's expert is a lane read (a vector load per unit would be waited
+    // for behind the weights already in flight).
     const int64_t b0 = s0 / spb;
-    const int bexp = b0 + lane < nused ? a.block_expert[b0 + lane] : -1;
+    const int bexp = b0 + lane < nused ? bexp_lds[b0 + lane] : -1;
     auto unit_of = [&](int64_t s, PxUnit<STAGE>& u) {
         u.b = s / spb;
         const int q = (int)(s - u.b * spb) * kPxWaves + wave;
