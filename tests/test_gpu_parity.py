@@ -649,6 +649,13 @@ def test_forward_monolithic_stages_and_replay(moe):
                                      stages=moe.MOE_STAGE_DOWN | moe.MOE_STAGE_COMBINE)
     torch.cuda.synchronize()
     assert torch.equal(bufs.out.view(torch.int16), ref.view(torch.int16))
+    # The one-token down + combine leaves its arrival counts at zero: the
+    # stage again on its own gives the same rows.
+    bufs.out.zero_()
+    moe.moe_a16w4_forward_monolithic(x, logits, *w, 6, bufs=bufs,
+                                     stages=moe.MOE_STAGE_DOWN | moe.MOE_STAGE_COMBINE)
+    torch.cuda.synchronize()
+    assert torch.equal(bufs.out.view(torch.int16), ref.view(torch.int16))
     with pytest.raises(moe.MoeError, match="stage mask"):
         moe.moe_a16w4_forward_monolithic(x, logits, *w, 6, bufs=bufs, stages=moe.MOE_STAGE_DOWN)
     side = torch.cuda.Stream()
