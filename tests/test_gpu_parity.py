@@ -603,6 +603,8 @@ MONO_CASES = [
     (1, 512, 384, 128, 64, 16, True, False),     # 128 experts, 64 slots, I = 384
     (1, 4096, 4096, 64, 7, 64, False, False),    # largest H and I, no renormalisation
     (1, 1024, 512, 1, 1, 16, True, True),        # a single expert
+    (1, 768, 1024, 64, 48, 16, True, False),     # 48 slots
+    (1, 4096, 256, 16, 4, 16, False, True),      # I = 256: one 64-lane chunk, 16 lanes busy
     (1, 512, 256, 200, 8, 16, True, False),      # more than 128 experts: routed separately
     (3, 512, 256, 16, 4, 16, True, True),        # several tokens: route_align + forward
 ]
@@ -649,8 +651,7 @@ def test_forward_monolithic_stages_and_replay(moe):
                                      stages=moe.MOE_STAGE_DOWN | moe.MOE_STAGE_COMBINE)
     torch.cuda.synchronize()
     assert torch.equal(bufs.out.view(torch.int16), ref.view(torch.int16))
-    # The one-token down + combine leaves its arrival counts at zero: the
-    # stage again on its own gives the same rows.
+    # The down + combine stage again on its own gives the same rows.
     bufs.out.zero_()
     moe.moe_a16w4_forward_monolithic(x, logits, *w, 6, bufs=bufs,
                                      stages=moe.MOE_STAGE_DOWN | moe.MOE_STAGE_COMBINE)
