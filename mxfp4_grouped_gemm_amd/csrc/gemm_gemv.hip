@@ -5,7 +5,8 @@
 // With one or a few activation rows per expert block, 15/16 of every MFMA
 // would idle and the MFMA operand layout (16 rows x 64 bytes per load) costs a
 // memory instruction per 64 bytes of each row. Here a wave owns 4 weight
-// rows over the whole K instead:
+// rows over the whole K instead (the down kernel at one token row: two sets
+// of 4):
 //  * each load instruction reads 1 KB contiguous of one row (lane l holds MX
 //    block 64c + l of chunk c), and every load of the wave is issued up
 //    front, so a wave is one memory round trip;
@@ -60,18 +61,23 @@ void stage1_gemv_kernel(MoeGemmArgs a) {
 }
 
 // Stage 2, block-major like stage 1: unit = (expert block b, output rows
-// n0..n0+3); a wave reads those 4 rows of the block's expert once (6 KB at
-// I = 3072, one memory round trip in half-block loads) and dots them with the
-// block's <= NRMAX h rows one after another, storing fp32 y[pair][n]; the
-// combine kernel follows. A workgroup covers kDownRows consecutive rows of one
-// block, so its loads are one contiguous run of the expert's rows.
-template <int NHC, int NRMAX>
+// n0..n0+4NS-1); a wave reads those rows of the block's expert once (NS sets
+// of 4 rows, 6 KB each at I = 3072, one memory round trip in half-block
+// loads) and dots them with the block's <= NRMAX h rows one after another,
+// storing fp32 y[pair][n]; the combine kernel follows. A workgroup covers
+// 4 NS kDownWaves consecutive rows of one block, so its loads are one
+// contiguous run of the expert's rows. One-row blocks take two sets per
+// wave (90 VGPRs, five waves per SIMD): twice the weight bytes in flight per
+// h row loaded (graph-replayed step, three alternating runs on one box: 58.2
+// -> 57.1 us at one token, 29.5 -> 28.9 us on the 8-way shard); four sets
+// (145 VGPRs) were slower.
+template <int NHC, int NRMAX, int NS>
 __global__ __launch_bounds__(kDownWaves * 64) void stage2_gemv_blk_kernel(MoeGemmArgs a) {
-    __shared__ __attribute__((aligned(16))) uint8_t lds_scale[kDownWaves][4 * 32 * NHC];
+    __shared__ __attribute__((aligned(16))) uint8_t lds_scale[kDownWaves][NS][4 * 32 * NHC];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar addressing
     const int H = a.H, I = a.I, nblk = I / 32, nhb = I / 16;
-    const int gpb = H / kDownRows;  // row groups per block
+    const int gpb = H / (NS * kDownRows);  // row groups per block
     const int64_t b = blockIdx.x / gpb;
     const int g = (int)(blockIdx.x % gpb);
     const int nused = *a.num_post_pad / a.bm;  // blocks holding pairs
@@ -85,16 +91,18 @@ __global__ __launch_bounds__(kDownWaves * 64) void stage2_gemv_blk_kernel(MoeGem
         pair[m] = a.sorted_ids[row0 + m];
         nvalid += (pair[m] >= 0 && pair[m] < P) ? 1 : 0;
     }
-    const int n0 = g * kDownRows + 4 * wave;
+    const int n0 = g * NS * kDownRows + 4 * NS * wave;
     if ((unsigned)e >= (unsigned)a.E) return;
     const rsrc_t rw = make_rsrc(a.w2 + (int64_t)e * H * (I / 2), (uint32_t)((int64_t)H * (I / 2)));
     const rsrc_t rs = make_rsrc((const uint8_t*)a.w2_scale + (int64_t)e * H * nblk, (uint32_t)((int64_t)H * nblk));
     const rsrc_t rx = make_rsrc(a.h, (uint32_t)((int64_t)P * I * 2));
     u32x4 x[NHC][2];
     issue_xh<NHC>(x, rx, nvalid > 0 ? (uint32_t)pair[0] * (uint32_t)(2 * I) : kOob, nhb, lane);
-    HalfRows<NHC> W;
-    W.issue_run(rw, rs, n0, 4, nhb, lane);
-    W.stage_scales(lds_scale[wave], nhb, lane);
+    HalfRows<NHC> W[NS];
+#pragma unroll
+    for (int k = 0; k < NS; ++k) W[k].issue_run(rw, rs, n0 + 4 * k, 4, nhb, lane);
+#pragma unroll
+    for (int k = 0; k < NS; ++k) W[k].stage_scales(lds_scale[wave][k], nhb, lane);
     wave_lds_sync();
     const int rho = lane >> 4;
     const int r = (rho == 1) ? 2 : (rho == 2) ? 1 : rho;  // rows after reduce4: (0, 2, 1, 3)
@@ -102,10 +110,13 @@ __global__ __launch_bounds__(kDownWaves * 64) void stage2_gemv_blk_kernel(MoeGem
     for (int m = 0; m < NRMAX; ++m) {
         if (m >= nvalid) break;
         if (m > 0) issue_xh<NHC>(x, rx, (uint32_t)pair[m] * (uint32_t)(2 * I), nhb, lane);
-        float acc[4] = {0.f, 0.f, 0.f, 0.f};
-        half_dot<NHC>(W, lds_scale[wave], x, nhb, lane, acc);
-        const float q = reduce4(acc);
-        if ((lane & 15) == 0) a.y[(int64_t)pair[m] * H + n0 + r] = q;
+#pragma unroll
+        for (int k = 0; k < NS; ++k) {
+            float acc[4] = {0.f, 0.f, 0.f, 0.f};
+            half_dot<NHC>(W[k], lds_scale[wave][k], x, nhb, lane, acc);
+            const float q = reduce4(acc);
+            if ((lane & 15) == 0) a.y[(int64_t)pair[m] * H + n0 + 4 * k + r] = q;
+        }
     }
 }
 
@@ -133,10 +144,12 @@ static void launch_stage1_nr(const MoeGemmArgs& a, int nch, hipStream_t s) {
 template <int NHC>
 static void launch_down_blk(const MoeGemmArgs& a, int rows, hipStream_t s) {
     const dim3 grid((unsigned)((a.cap / a.bm) * (a.H / kDownRows))), block(kDownWaves * 64);
-    if (rows <= 1) hipLaunchKernelGGL((stage2_gemv_blk_kernel<NHC, 1>), grid, block, 0, s, a);
-    else if (rows <= 2) hipLaunchKernelGGL((stage2_gemv_blk_kernel<NHC, 2>), grid, block, 0, s, a);
-    else if (rows <= 4) hipLaunchKernelGGL((stage2_gemv_blk_kernel<NHC, 4>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((stage2_gemv_blk_kernel<NHC, 8>), grid, block, 0, s, a);
+    if (rows <= 1 && a.H % (2 * kDownRows) == 0)
+        hipLaunchKernelGGL((stage2_gemv_blk_kernel<NHC, 1, 2>), dim3(grid.x / 2), block, 0, s, a);
+    else if (rows <= 1) hipLaunchKernelGGL((stage2_gemv_blk_kernel<NHC, 1, 1>), grid, block, 0, s, a);
+    else if (rows <= 2) hipLaunchKernelGGL((stage2_gemv_blk_kernel<NHC, 2, 1>), grid, block, 0, s, a);
+    else if (rows <= 4) hipLaunchKernelGGL((stage2_gemv_blk_kernel<NHC, 4, 1>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((stage2_gemv_blk_kernel<NHC, 8, 1>), grid, block, 0, s, a);
 }
 
 hipError_t launch_gemv_stage(const MoeGemmArgs& a, int stage, hipStream_t s) {
