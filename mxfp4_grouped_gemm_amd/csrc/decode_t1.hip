@@ -89,30 +89,56 @@ __device__ __forceinline__ void t1_write_outputs(const MoeGemmArgs& a, const int
 // the ranks that route_token<2> computes (for each expert, the number of
 // experts ordered before it: larger logit, or equal and lower index), with
 // the count split over the waves (wave q compares against entries
-// 32q .. 32q + 31) and summed in LDS, then wave 0 forms the same softmax
-// terms in the same order as route_token<2>, so ids and weights are
-// bit-identical to it. Leaves sid[rank] / swt[rank] in LDS for rank < topk.
-// Every thread of the workgroup must call it.
+// kPer q .. kPer q + kPer - 1, kPer = 128 / kT1Waves) and summed in LDS,
+// then wave 0 forms the same softmax terms in the same order as
+// route_token<2>, so ids and weights are bit-identical to it. Leaves
+// sid[rank] / swt[rank] in LDS for rank < topk. Every thread of the
+// workgroup must call it. With six workgroups per CU routing at once the
+// count is VALU-bound (per-workgroup clocks: 1.3 us of a 2.8 us routing);
+// a radix select over ballots in wave 0 alone was slower (3.1 us: sixteen
+// dependent rounds), and so were 8-wave workgroups (three per CU).
 struct T1RouteLds {
     uint64_t key[128];
     int32_t prank[kT1Waves][128];
 };
 
+// The 64-lane sum with the pairing of a xor butterfly over lane offsets 32,
+// 16, 8, 4, 2, 1 -- the partial sums of the shuffle loop of the routing
+// routine, so the same bits -- by register swaps and DPP rotations (after
+// the first two steps a row's values are symmetric under xor 8, so a
+// rotation by 8, 4, 2, 1 meets the xor partner) instead of six LDS permutes.
+__device__ __forceinline__ float wave_sum_butterfly(float v) {
+    float a = v, b = v;
+    permlane32_swap(a, b);
+    v = a + b;
+    a = v;
+    b = v;
+    permlane16_swap(a, b);
+    return row16_sum(a + b);
+}
+
 __device__ __forceinline__ void t1_route(const float* __restrict__ row, int E, int topk, int renorm,
                                          T1RouteLds& r, int32_t* sid, float* swt, int wave, int lane) {
+    constexpr int kPer = 128 / kT1Waves;  // entries each wave ranks against
     float val[2];
     uint64_t k64[2];
+    // Both logits of the lane in one round trip (branch-free loads).
+    const rsrc_t rl = make_rsrc(row, (uint32_t)E * 4u);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int e = lane + 64 * i;
-        val[i] = e < E ? row[e] : 0.0f;
+        val[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, e < E ? 4u * (uint32_t)e : kOob, 0, 0));
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int e = lane + 64 * i;
         k64[i] = e < E ? ((uint64_t)route_key(val[i]) << 32) | (uint64_t)~(uint32_t)e : 0ull;
         if (wave == 0) r.key[e] = k64[i];
     }
     __syncthreads();
     int part[2] = {0, 0};
 #pragma unroll
-    for (int j = 32 * wave; j < 32 * wave + 32; j += 2) {
+    for (int j = kPer * wave; j < kPer * wave + kPer; j += 2) {
         const uint64_t kj0 = r.key[j], kj1 = r.key[j + 1];
 #pragma unroll
         for (int i = 0; i < 2; ++i) part[i] += (kj0 > k64[i] ? 1 : 0) + (kj1 > k64[i] ? 1 : 0);
@@ -127,7 +153,9 @@ __device__ __forceinline__ void t1_route(const float* __restrict__ row, int E, i
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int e = lane + 64 * i;
-            rank[i] = r.prank[0][e] + r.prank[1][e] + r.prank[2][e] + r.prank[3][e];
+            rank[i] = 0;
+#pragma unroll
+            for (int w = 0; w < kT1Waves; ++w) rank[i] += r.prank[w][e];
             sel[i] = e < E && rank[i] < topk;
             if (sel[i] && rank[i] == 0) kmax = (uint32_t)(k64[i] >> 32);
         }
@@ -141,8 +169,7 @@ __device__ __forceinline__ void t1_route(const float* __restrict__ row, int E, i
             ex[i] = ok ? expf(val[i] - lmax) : 0.0f;
             if (renorm ? sel[i] : ok) psum += ex[i];
         }
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) psum += __shfl_xor(psum, off);
+        psum = wave_sum_butterfly(psum);
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             if (sel[i]) {
@@ -223,9 +250,10 @@ hipError_t launch_t1_layer(const MoeGemmArgs& a, const float* logits, int renorm
                       ? n
                       : 256;
         }
-        // One round of resident workgroups (6 waves per SIMD: 6 per CU).
+        // One round of resident workgroups (6 waves per SIMD: 24 per CU).
+        constexpr int kPerCu = 24 / kT1Waves;
         const int64_t wgs = ((int64_t)a.topk * (a.I / 2) + kT1Waves - 1) / kT1Waves;
-        const dim3 grid((unsigned)(wgs < 6 * cus ? wgs : 6 * cus)), block(kT1Waves * 64);
+        const dim3 grid((unsigned)(wgs < kPerCu * cus ? wgs : kPerCu * cus)), block(kT1Waves * 64);
         const int nch = (a.H / 32 + 63) / 64;
         const bool epi = a.w13_bias || a.swiglu_limit > 0.0f;
 #define MOE_T1A(NC, EP) hipLaunchKernelGGL((route_gate_up_t1_kernel<NC, EP>), grid, block, 0, s, b, logits, renorm, o)
