@@ -66,11 +66,13 @@ void stage1_gemv_kernel(MoeGemmArgs a) {
 // loads) and dots them with the block's <= NRMAX h rows one after another,
 // storing fp32 y[pair][n]; the combine kernel follows. A workgroup covers
 // 4 NS kDownWaves consecutive rows of one block, so its loads are one
-// contiguous run of the expert's rows. One-row blocks take two sets per
-// wave (90 VGPRs, five waves per SIMD): twice the weight bytes in flight per
+// contiguous run of the expert's rows. Two sets per wave (90 VGPRs at one
+// token row, five waves per SIMD) put twice the weight bytes in flight per
 // h row loaded (graph-replayed step, three alternating runs on one box: 58.2
-// -> 57.1 us at one token, 29.5 -> 28.9 us on the 8-way shard); four sets
-// (145 VGPRs) were slower.
+// -> 57.1 us at one token, 29.5 -> 28.9 us on the 8-way shard; blocks of up
+// to 4 and 8 rows at the production shape, forced onto this kernel: 58.4 ->
+// 53.9 us at 4 tokens, 87.5 -> 84.7 us at 7); four sets (145 VGPRs) were
+// slower.
 template <int NHC, int NRMAX, int NS>
 __global__ __launch_bounds__(kDownWaves * 64) void stage2_gemv_blk_kernel(MoeGemmArgs a) {
     __shared__ __attribute__((aligned(16))) uint8_t lds_scale[kDownWaves][NS][4 * 32 * NHC];
@@ -141,15 +143,15 @@ static void launch_stage1_nr(const MoeGemmArgs& a, int nch, hipStream_t s) {
     }
 }
 
+// Two sets of 4 rows per wave: H is a multiple of 256 on this path, so a
+// workgroup's 32 rows divide it.
 template <int NHC>
 static void launch_down_blk(const MoeGemmArgs& a, int rows, hipStream_t s) {
-    const dim3 grid((unsigned)((a.cap / a.bm) * (a.H / kDownRows))), block(kDownWaves * 64);
-    if (rows <= 1 && a.H % (2 * kDownRows) == 0)
-        hipLaunchKernelGGL((stage2_gemv_blk_kernel<NHC, 1, 2>), dim3(grid.x / 2), block, 0, s, a);
-    else if (rows <= 1) hipLaunchKernelGGL((stage2_gemv_blk_kernel<NHC, 1, 1>), grid, block, 0, s, a);
-    else if (rows <= 2) hipLaunchKernelGGL((stage2_gemv_blk_kernel<NHC, 2, 1>), grid, block, 0, s, a);
-    else if (rows <= 4) hipLaunchKernelGGL((stage2_gemv_blk_kernel<NHC, 4, 1>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((stage2_gemv_blk_kernel<NHC, 8, 1>), grid, block, 0, s, a);
+    const dim3 grid((unsigned)((a.cap / a.bm) * (a.H / (2 * kDownRows)))), block(kDownWaves * 64);
+    if (rows <= 1) hipLaunchKernelGGL((stage2_gemv_blk_kernel<NHC, 1, 2>), grid, block, 0, s, a);
+    else if (rows <= 2) hipLaunchKernelGGL((stage2_gemv_blk_kernel<NHC, 2, 2>), grid, block, 0, s, a);
+    else if (rows <= 4) hipLaunchKernelGGL((stage2_gemv_blk_kernel<NHC, 4, 2>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((stage2_gemv_blk_kernel<NHC, 8, 2>), grid, block, 0, s, a);
 }
 
 hipError_t launch_gemv_stage(const MoeGemmArgs& a, int stage, hipStream_t s) {
