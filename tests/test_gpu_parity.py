@@ -606,6 +606,9 @@ MONO_CASES = [
     (1, 768, 1024, 64, 48, 16, True, False),     # 48 slots
     (1, 4096, 256, 16, 4, 16, False, True),      # I = 256: one 64-lane chunk, 16 lanes busy
     (1, 512, 256, 200, 8, 16, True, False),      # more than 128 experts: routed separately
+    (1, 3584, 384, 896, 15, 16, True, False),    # the 8-way tensor-parallel shard (routed separately)
+    (1, 768, 256, 1024, 64, 16, False, False),   # 1024 experts, 64 slots, no renormalisation
+    (1, 512, 256, 129, 5, 32, True, True),       # 129 experts, biases, 32-row blocks
     (3, 512, 256, 16, 4, 16, True, True),        # several tokens: route_align + forward
 ]
 
@@ -634,6 +637,30 @@ def test_forward_monolithic(moe, T, H, I, E, topk, bm, renorm, bias):
     ref = oracle.moe_forward(wl.x, wl.w13, wl.w13_scale, wl.w2, wl.w2_scale, 0, rids, rw, I=I,
                              w13_bias=b13, w2_bias=b2, swiglu_limit=100.0 if bias else 0.0)
     check_close(out_f64(bufs.out), ref, f"monolithic T={T} H={H} I={I} E={E} k={topk} bm={bm} renorm={renorm} bias={bias}")
+
+
+@pytest.mark.parametrize("E,topk", [(112, 15), (300, 20), (1024, 64)])
+def test_forward_monolithic_tied_logits(moe, E, topk):
+    """One token whose logits take a few values only (many ties, broken by
+    the lower index): the monolithic call (routing inside gate_up up to 128
+    experts, the one-token routing kernel above) gives the standalone
+    routing's ids, weights and align/sort arrays bit for bit, and the
+    oracle's ids."""
+    wl = synth.small(T=1, H=512, I=256, E=E, topk=topk, seed=E + topk, scale_lo=118, scale_hi=128)
+    logits = np.round(wl.logits * 2.0).astype(np.float32) / 2.0
+    w = weights_dev(wl)
+    lg = dev(logits)
+    bufs = moe.moe_a16w4_forward_monolithic(x_dev(wl), lg, *w, topk)
+    ids, wts, srt, be, off, npp = moe.moe_route_align(lg, topk, E, 16)
+    torch.cuda.synchronize()
+    for name, got, want in (("ids", bufs.ids, ids), ("weights", bufs.weights, wts), ("sorted_ids", bufs.sorted_ids, srt),
+                            ("block_expert", bufs.block_expert, be), ("expert_offsets", bufs.expert_offsets, off),
+                            ("num_post_pad", bufs.num_post_pad, npp)):
+        assert torch.equal(got.view(torch.int32), want.view(torch.int32)), name
+    rids, rw = oracle.route_topk(logits, topk, renormalize=True)
+    assert np.array_equal(bufs.ids.cpu().numpy().reshape(rids.shape), rids)
+    ref = oracle.moe_forward(wl.x, wl.w13, wl.w13_scale, wl.w2, wl.w2_scale, 0, rids, rw, I=256)
+    check_close(out_f64(bufs.out), ref, f"monolithic tied logits E={E} k={topk}")
 
 
 def test_forward_monolithic_stages_and_replay(moe):
