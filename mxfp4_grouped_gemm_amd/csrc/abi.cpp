@@ -170,7 +170,7 @@ moe_status launch_route_align_any(const float* logits, int T, int E, int topk, i
             moe::launch_route_topk(logits, T, E, topk, renormalize, topk_ids, topk_weights, s), fn);
         if (st != MOE_OK) return st;
     }
-    return hip_status(moe::launch_align_sort(topk_ids, (int)P, E, block_m, cap, sorted_ids, block_expert,
+    return hip_status(moe::launch_align_sort(topk_ids, (int)P, topk, E, block_m, cap, sorted_ids, block_expert,
                                              expert_offsets, num_post_pad, s),
                       fn);
 }
@@ -260,7 +260,7 @@ moe_status moe_align_sort(const int32_t* topk_ids, int T, int topk, int E, int b
     if (!aligned(topk_ids, 4) || !aligned(sorted_ids, 4) || !aligned(block_expert, 4) ||
         !aligned(expert_offsets, 4) || !aligned(num_post_pad, 4))
         return fail(MOE_ERR_INVALID_ARG, "moe_align_sort: misaligned pointer");
-    return hip_status(moe::launch_align_sort(topk_ids, (int)P, E, block_m, cap, sorted_ids, block_expert,
+    return hip_status(moe::launch_align_sort(topk_ids, (int)P, topk, E, block_m, cap, sorted_ids, block_expert,
                                              expert_offsets, num_post_pad, (hipStream_t)stream),
                       "moe_align_sort");
 }

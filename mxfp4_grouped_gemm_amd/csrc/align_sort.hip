@@ -5,11 +5,17 @@
 // the grouping rule itself is the plain stable one.
 //
 // One 1024-thread workgroup. Counts come from LDS atomic adds (order does
-// not matter for a count). Positions never come from atomic order: pairs
-// are processed in tiles of 1024, each wave ORs one bit per pair into a
-// per-(wave, expert) 64-bit mask, and a pair's rank is the popcount of the
-// bits below it plus the counts of earlier waves and tiles -- a stable
-// counting sort, bit-identical run to run.
+// not matter for a count). Positions never come from atomic order. When
+// every token's pairs name distinct experts (the routing's always do), a
+// token-by-expert bit matrix in LDS (bit t of expert e's row set when token
+// t chose e) gives each pair its rank directly: the set bits of its
+// expert's row below its token, from a per-word prefix of the row, so the
+// pairs are placed in one pass (at 1024 tokens x 15 slots: 29 -> 5 us, see
+// the launcher). Otherwise (a token naming an expert twice, or a matrix too
+// large for the LDS) pairs are processed in tiles of 1024, each wave ORs one
+// bit per pair into a per-(wave, expert) 64-bit mask, and a pair's rank is
+// the popcount of the bits below it plus the counts of earlier waves and
+// tiles. Both are the stable counting sort, bit-identical run to run.
 //
 // route_align_kernel runs the routing of up to 64 tokens (route.hpp, one
 // wave per token) in the same workgroup and sorts straight from LDS, saving
@@ -28,28 +34,24 @@ constexpr int kMaxExperts = 1024;
 constexpr int kFusedMaxPairs = 4096;
 
 struct SortShared {
-    unsigned long long masks[kSortWaves * kMaxExperts];
+    unsigned long long masks[kSortWaves * kMaxExperts];  // or the bit matrix, its prefixes and the sorted rows
     int counts[kMaxExperts];
     int running[kMaxExperts];
     int offs[kMaxExperts + 1];
+    int nvalid, nbits;
 };
+// 32-bit words of the mask table, which the token bit matrix path reuses.
+constexpr int kBitWords = kSortWaves * kMaxExperts * 2;
 
-// ids: global or LDS (generic pointer).
-__device__ void align_sort_body(SortShared& sh, const int32_t* ids, int P, int E, int bm, int64_t cap,
-                                int32_t* __restrict__ sorted_ids, int32_t* __restrict__ block_expert,
-                                int32_t* __restrict__ expert_offsets,
-                                int32_t* __restrict__ num_post_pad) {
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wv = tid >> 6;
-
-    for (int e = tid; e < E; e += kSortThreads) {
-        sh.counts[e] = 0;
-        sh.running[e] = 0;
-    }
-    __syncthreads();
-    // Eight ids per thread in flight (clamped index, no branch), then the
-    // counts: one memory round trip per 8192 pairs instead of per 1024.
+// Eight ids per thread in flight (clamped index, no branch): one memory round
+// trip per 8192 pairs instead of per 1024. f(p, t, e) for every pair p =
+// t * topk + slot, e = -1 past P; the token index advances by the stride
+// (no integer division per pair: at 15 pairs per thread the divisions alone
+// took microseconds).
+template <class F>
+__device__ __forceinline__ void for_each_id(const int32_t* ids, int P, int topk, int tid, F&& f) {
+    const int dq = kSortThreads / topk, dr = kSortThreads % topk;
+    int t = tid / topk, r = tid % topk;
     for (int base = 0; base < P; base += 8 * kSortThreads) {
         int ev[8];
 #pragma unroll
@@ -59,10 +61,121 @@ __device__ void align_sort_body(SortShared& sh, const int32_t* ids, int P, int E
             if (p >= P) ev[u] = -1;
         }
 #pragma unroll
-        for (int u = 0; u < 8; ++u)
-            if ((unsigned)ev[u] < (unsigned)E) atomicAdd(&sh.counts[ev[u]], 1);
+        for (int u = 0; u < 8; ++u) {
+            f(base + u * kSortThreads + tid, t, ev[u]);
+            t += dq;
+            r += dr;
+            if (r >= topk) {
+                r -= topk;
+                ++t;
+            }
+        }
+    }
+}
+
+// ids: global or LDS (generic pointer).
+// Inlined into each kernel, so that the LDS tables are addressed as LDS (a
+// called function saw generic pointers: flat instructions, and the old
+// tiled pass took 29 us at 15,360 pairs).
+__device__ __forceinline__ void align_sort_body(SortShared& sh, const int32_t* ids, int P, int topk, int E,
+                                                int bm, int64_t cap, int32_t* __restrict__ sorted_ids,
+                                                int32_t* __restrict__ block_expert,
+                                                int32_t* __restrict__ expert_offsets,
+                                                int32_t* __restrict__ num_post_pad) {
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wv = tid >> 6;
+    // Token bit matrix: row e (W words) holds bit t for token t = p / topk;
+    // then the rows' prefixes and the sorted rows themselves, written to
+    // LDS and copied out in order (scattered 4-byte stores from one CU took
+    // half of the pass at 15,360 pairs). The pairs' ids stay in registers
+    // (kFastIds per thread) from one round trip to the placement.
+    // Rows are RS words apart, RS odd, so the words of one token column in
+    // different rows fall in different LDS banks (a stride of 32 words put
+    // every row's word in one bank: the atomics of a wave serialised).
+    // The sorted rows sit at r + r / 32 (segment starts are multiples of the
+    // block, so unpadded their stores would fall in two banks).
+    constexpr int kFastIds = 16;
+    const int W = (P / topk + 31) / 32, RS = W | 1;
+    bool fast = P <= kFastIds * kSortThreads && 2 * (int64_t)E * RS + cap + cap / 32 + 1 <= kBitWords;
+    uint32_t* const bits = (uint32_t*)sh.masks;
+    uint32_t* const pre = bits + E * RS;
+    int32_t* const srt = (int32_t*)(pre + E * RS);
+
+    for (int e = tid; e < E; e += kSortThreads) {
+        sh.counts[e] = 0;
+        sh.running[e] = 0;
+    }
+    if (tid == 0) sh.nvalid = sh.nbits = 0;
+    if (fast) {
+        for (int i = tid; i < E * RS; i += kSortThreads) bits[i] = 0u;
+        for (int i = tid; i < (int)(cap + cap / 32 + 1); i += kSortThreads) srt[i] = P;
+    }
+    // Pair k of this thread: p = k * kSortThreads + tid, token tv[k].
+    int ev[kFastIds], tv[kFastIds];
+    if (fast) {
+        const int dq = kSortThreads / topk, dr = kSortThreads % topk;
+        int t = tid / topk, r = tid % topk;
+#pragma unroll
+        for (int k = 0; k < kFastIds; ++k) {
+            const int p = k * kSortThreads + tid;
+            ev[k] = p < P ? ids[p] : -1;
+            tv[k] = t;
+            t += dq;
+            r += dr;
+            if (r >= topk) {
+                r -= topk;
+                ++t;
+            }
+        }
     }
     __syncthreads();
+    if (fast) {
+        // Bits only (no count atomics, no returned values): a token naming an
+        // expert twice sets one bit for two pairs, which the totals below
+        // detect.
+        int nv = 0;
+#pragma unroll
+        for (int k = 0; k < kFastIds; ++k) {
+            const int e = ev[k], t = tv[k];
+            if ((unsigned)e < (unsigned)E) {
+                atomicOr(&bits[e * RS + (t >> 5)], 1u << (t & 31));
+                ++nv;
+            }
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) nv += __shfl_xor(nv, off);
+        if (lane == 0) atomicAdd(&sh.nvalid, nv);
+        __syncthreads();
+        // Row prefixes: a thread per row, eight words read at a time.
+        for (int e = tid; e < E; e += kSortThreads) {
+            int run = 0;
+            for (int w0 = 0; w0 < W; w0 += 8) {
+                uint32_t v[8];
+#pragma unroll
+                for (int k = 0; k < 8; ++k) v[k] = w0 + k < W ? bits[e * RS + w0 + k] : 0u;
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    if (w0 + k < W) pre[e * RS + w0 + k] = run;
+                    run += __popc(v[k]);
+                }
+            }
+            sh.counts[e] = run;
+            atomicAdd(&sh.nbits, run);
+        }
+        __syncthreads();
+        fast = sh.nbits == sh.nvalid;
+        if (!fast) {
+            for (int e = tid; e < E; e += kSortThreads) sh.counts[e] = 0;
+            __syncthreads();
+        }
+    }
+    if (!fast) {
+        for_each_id(ids, P, topk, tid, [&](int, int, int e) {
+            if ((unsigned)e < (unsigned)E) atomicAdd(&sh.counts[e], 1);
+        });
+        __syncthreads();
+    }
 
     // Exclusive scan of the padded segment lengths (wave 0, 64 at a time).
     if (wv == 0) {
@@ -88,15 +201,34 @@ __device__ void align_sort_body(SortShared& sh, const int32_t* ids, int P, int E
     for (int e = tid; e <= E; e += kSortThreads) expert_offsets[e] = sh.offs[e];
     if (tid == 0) num_post_pad[0] = total;
 
-    // Padding rows of every segment, block -> expert map, and the unused tail.
-    // These rows are disjoint from the rows the scatter below writes.
+    // Block -> expert map, padding rows of every segment and the unused
+    // tail (the padding is already in the LDS rows on the bit matrix path).
     for (int e = wv; e < E; e += kSortWaves) {
         const int start = sh.offs[e], end = sh.offs[e + 1], c = sh.counts[e];
-        for (int r = start + c + lane; r < end; r += 64) sorted_ids[r] = P;
+        if (!fast)
+            for (int r = start + c + lane; r < end; r += 64) sorted_ids[r] = P;
         for (int b = start / bm + lane; b < end / bm; b += 64) block_expert[b] = e;
     }
-    for (int64_t r = total + tid; r < cap; r += kSortThreads) sorted_ids[r] = P;
+    if (!fast)
+        for (int64_t r = total + tid; r < cap; r += kSortThreads) sorted_ids[r] = P;
     for (int64_t b = total / bm + tid; b < cap / bm; b += kSortThreads) block_expert[b] = -1;
+
+    if (fast) {
+        // Pair p of token t and expert e ranks after the tokens before t
+        // that chose e: its row's prefix plus the set bits below t.
+#pragma unroll
+        for (int k = 0; k < kFastIds; ++k) {
+            const int e = ev[k], t = tv[k];
+            if ((unsigned)e < (unsigned)E) {
+                const int w = e * RS + (t >> 5);
+                const int r = sh.offs[e] + pre[w] + __popc(bits[w] & ((1u << (t & 31)) - 1u));
+                srt[r + (r >> 5)] = k * kSortThreads + tid;
+            }
+        }
+        __syncthreads();
+        for (int r = tid; r < (int)cap; r += kSortThreads) sorted_ids[r] = srt[r + (r >> 5)];
+        return;
+    }
 
     // Stable scatter, 1024 pairs per tile; the next tile's id is loaded
     // while this one is placed.
@@ -128,11 +260,11 @@ __device__ void align_sort_body(SortShared& sh, const int32_t* ids, int P, int E
 }
 
 __global__ __launch_bounds__(kSortThreads) void align_sort_kernel(
-    const int32_t* __restrict__ ids, int P, int E, int bm, int64_t cap,
+    const int32_t* __restrict__ ids, int P, int topk, int E, int bm, int64_t cap,
     int32_t* __restrict__ sorted_ids, int32_t* __restrict__ block_expert,
     int32_t* __restrict__ expert_offsets, int32_t* __restrict__ num_post_pad) {
     __shared__ SortShared sh;
-    align_sort_body(sh, ids, P, E, bm, cap, sorted_ids, block_expert, expert_offsets, num_post_pad);
+    align_sort_body(sh, ids, P, topk, E, bm, cap, sorted_ids, block_expert, expert_offsets, num_post_pad);
 }
 
 template <int VPL>
@@ -151,7 +283,7 @@ __global__ __launch_bounds__(kSortThreads) void route_align_kernel(
                          weights + (int64_t)t * topk, ids_lds + t * topk,
                          reinterpret_cast<uint64_t*>(sh.masks) + wv * 128);
     __syncthreads();
-    align_sort_body(sh, ids_lds, T * topk, E, bm, cap, sorted_ids, block_expert, expert_offsets,
+    align_sort_body(sh, ids_lds, T * topk, topk, E, bm, cap, sorted_ids, block_expert, expert_offsets,
                     num_post_pad);
 }
 
@@ -243,10 +375,10 @@ __global__ __launch_bounds__(NW * 64) void route_align_small_kernel(
     for (int i = tid; i < nblk; i += NT) block_expert[i] = blk[i];
 }
 
-hipError_t launch_align_sort(const int32_t* ids, int P, int E, int bm, int64_t cap,
+hipError_t launch_align_sort(const int32_t* ids, int P, int topk, int E, int bm, int64_t cap,
                              int32_t* sorted_ids, int32_t* block_expert, int32_t* expert_offsets,
                              int32_t* num_post_pad, hipStream_t s) {
-    hipLaunchKernelGGL(align_sort_kernel, dim3(1), dim3(kSortThreads), 0, s, ids, P, E, bm, cap,
+    hipLaunchKernelGGL(align_sort_kernel, dim3(1), dim3(kSortThreads), 0, s, ids, P, topk, E, bm, cap,
                        sorted_ids, block_expert, expert_offsets, num_post_pad);
     return hipGetLastError();
 }

@@ -11,7 +11,7 @@ namespace moe {
 hipError_t launch_route_topk(const float* logits, int T, int E, int topk, int renorm, int32_t* ids,
                              float* weights, hipStream_t s);
 
-hipError_t launch_align_sort(const int32_t* ids, int P, int E, int bm, int64_t cap,
+hipError_t launch_align_sort(const int32_t* ids, int P, int topk, int E, int bm, int64_t cap,
                              int32_t* sorted_ids, int32_t* block_expert, int32_t* expert_offsets,
                              int32_t* num_post_pad, hipStream_t s);
 

@@ -244,6 +244,38 @@ def test_route_align_one_token_many_experts(moe, E, topk, renorm, ties):
     assert np.array_equal(off.cpu().numpy(), roff)
 
 
+@pytest.mark.parametrize("T,E,topk,bm", [(64, 8, 4, 16), (1024, 112, 15, 32), (300, 1000, 8, 64)])
+def test_align_sort_repeated_experts(moe, T, E, topk, bm):
+    """Ids with a token naming one expert more than once (drawn with
+    replacement) take the tiled scatter instead of the token bit matrix;
+    the result is the same stable counting sort."""
+    rng = np.random.default_rng(T + E)
+    ids = rng.integers(0, E, size=(T, topk)).astype(np.int32)
+    ids[:, 1] = ids[:, 0]  # every token names its first expert twice
+    s, be, off, npp = moe.moe_align_sort(dev(ids), E, bm)
+    torch.cuda.synchronize()
+    rs, rbe, roff, rnpp = oracle.align_sort(ids, E, bm)
+    cap = len(rs)
+    assert int(npp.item()) == rnpp
+    assert np.array_equal(s.cpu().numpy()[:cap], rs)
+    assert np.array_equal(be.cpu().numpy()[:cap // bm], rbe)
+    assert np.array_equal(off.cpu().numpy(), roff)
+
+
+@pytest.mark.parametrize("T,E,topk", [(5000, 600, 4), (40000, 16, 2)])
+def test_align_sort_large_bit_matrix(moe, T, E, topk):
+    """Token bit matrices larger than the LDS table (E x T / 32 words) take
+    the tiled scatter; same result."""
+    ids = _sort_case(T, E, topk, seed=T + E)
+    s, be, off, npp = moe.moe_align_sort(dev(ids), E, 64)
+    torch.cuda.synchronize()
+    rs, rbe, roff, rnpp = oracle.align_sort(ids, E, 64)
+    cap = len(rs)
+    assert int(npp.item()) == rnpp
+    assert np.array_equal(s.cpu().numpy()[:cap], rs)
+    assert np.array_equal(off.cpu().numpy(), roff)
+
+
 def test_align_sort_drops_out_of_range_ids(moe):
     ids = np.array([[0, 5], [9, 1], [-1, 3]], dtype=np.int32)
     s, be, off, npp = moe.moe_align_sort(dev(ids), 6, 16)
