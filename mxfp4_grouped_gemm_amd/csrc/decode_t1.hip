@@ -102,21 +102,6 @@ struct T1RouteLds {
     int32_t prank[kT1Waves][128];
 };
 
-// The 64-lane sum with the pairing of a xor butterfly over lane offsets 32,
-// 16, 8, 4, 2, 1 -- the partial sums of the shuffle loop of the routing
-// routine, so the same bits -- by register swaps and DPP rotations (after
-// the first two steps a row's values are symmetric under xor 8, so a
-// rotation by 8, 4, 2, 1 meets the xor partner) instead of six LDS permutes.
-__device__ __forceinline__ float wave_sum_butterfly(float v) {
-    float a = v, b = v;
-    permlane32_swap(a, b);
-    v = a + b;
-    a = v;
-    b = v;
-    permlane16_swap(a, b);
-    return row16_sum(a + b);
-}
-
 __device__ __forceinline__ void t1_route(const float* __restrict__ row, int E, int topk, int renorm,
                                          T1RouteLds& r, int32_t* sid, float* swt, int wave, int lane) {
     constexpr int kPer = 128 / kT1Waves;  // entries each wave ranks against

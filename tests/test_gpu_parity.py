@@ -113,10 +113,20 @@ def test_route_matches_oracle(moe, name, _):
 
 @pytest.mark.parametrize("T,E,topk,renorm,ties", [(5, 200, 7, True, False), (3, 1024, 64, True, False),
                                                   (9, 64, 64, False, False), (6, 30, 5, True, True),
-                                                  (33, 1, 1, True, False), (4, 112, 15, False, False)])
+                                                  (33, 1, 1, True, False), (4, 112, 15, False, False),
+                                                  (8, 112, 15, True, True), (5, 128, 40, False, True),
+                                                  (4, 128, 64, True, True), (6, 112, 15, True, "zeros"),
+                                                  (3, 97, 1, True, False), (7, 120, 48, True, True)])
 def test_route_edge_cases(moe, T, E, topk, renorm, ties):
+    """Ties at the top-k boundary (integer logits), the candidate threshold
+    at up to 128 experts with few and with many candidates, and +0 / -0 logits
+    (equal keys: lower index first)."""
     rng = np.random.default_rng(T * 7 + E)
-    if ties:
+    if ties == "zeros":
+        logits = rng.integers(-1, 2, size=(T, E)).astype(np.float32)
+        logits[rng.random((T, E)) < 0.5] *= np.float32(0.0)   # signed zeros from -1 and +1
+        logits[rng.random((T, E)) < 0.3] = np.float32(-0.0)
+    elif ties:
         logits = rng.integers(-2, 3, size=(T, E)).astype(np.float32)
     else:
         logits = rng.standard_normal((T, E)).astype(np.float32) * 3
