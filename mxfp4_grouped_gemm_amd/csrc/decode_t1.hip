@@ -85,74 +85,77 @@ __device__ __forceinline__ void t1_write_outputs(const MoeGemmArgs& a, const int
     for (int i = lane; i < topk * bm; i += 64) o.sorted_ids[i] = (i % bm == 0) ? blk_j[i / bm] : topk;
 }
 
-// Routes the token for a workgroup of kT1Waves waves (E <= 128, topk <= 64):
-// the ranks that route_token<2> computes (for each expert, the number of
-// experts ordered before it: larger logit, or equal and lower index), with
-// the count split over the waves (wave q compares against entries
-// kPer q .. kPer q + kPer - 1, kPer = 128 / kT1Waves) and summed in LDS,
-// then wave 0 forms the same softmax terms in the same order as
-// route_token<2>, so ids and weights are bit-identical to it. Leaves
-// sid[rank] / swt[rank] in LDS for rank < topk. Every thread of the
-// workgroup must call it. With six workgroups per CU routing at once the
-// count is VALU-bound (per-workgroup clocks: 1.3 us of a 2.8 us routing);
-// a radix select over ballots in wave 0 alone was slower (3.1 us: sixteen
-// dependent rounds), and so were 8-wave workgroups (three per CU).
+// Routes the token for a workgroup (E <= 128, topk <= 64), in wave 0 alone:
+// the selection and ranks of route_token<2> (a candidate threshold from one
+// round of guesses, then each candidate ranked against the candidates in
+// LDS by (key, ~index)) and the same softmax terms summed in the same order,
+// so ids and weights are bit-identical to it. Leaves sid[rank] / swt[rank]
+// in LDS for rank < topk. Every thread of the workgroup must call it.
+// Per-workgroup clocks: routing 1.8-2.6 us (median over the launch) against
+// 2.4-2.8 us for every expert counted against every key with the count
+// split over the four waves (VALU-bound with six workgroups per CU routing
+// at once), and 2.3-3.1 us with radix rounds in place of the guesses.
 struct T1RouteLds {
     uint64_t key[128];
-    int32_t prank[kT1Waves][128];
 };
 
 __device__ __forceinline__ void t1_route(const float* __restrict__ row, int E, int topk, int renorm,
                                          T1RouteLds& r, int32_t* sid, float* swt, int wave, int lane) {
-    constexpr int kPer = 128 / kT1Waves;  // entries each wave ranks against
-    float val[2];
-    uint64_t k64[2];
-    // Both logits of the lane in one round trip (branch-free loads).
-    const rsrc_t rl = make_rsrc(row, (uint32_t)E * 4u);
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int e = lane + 64 * i;
-        val[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, e < E ? 4u * (uint32_t)e : kOob, 0, 0));
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int e = lane + 64 * i;
-        k64[i] = e < E ? ((uint64_t)route_key(val[i]) << 32) | (uint64_t)~(uint32_t)e : 0ull;
-        if (wave == 0) r.key[e] = k64[i];
-    }
-    __syncthreads();
-    int part[2] = {0, 0};
-#pragma unroll
-    for (int j = kPer * wave; j < kPer * wave + kPer; j += 2) {
-        const uint64_t kj0 = r.key[j], kj1 = r.key[j + 1];
-#pragma unroll
-        for (int i = 0; i < 2; ++i) part[i] += (kj0 > k64[i] ? 1 : 0) + (kj1 > k64[i] ? 1 : 0);
-    }
-    r.prank[wave][lane] = part[0];
-    r.prank[wave][lane + 64] = part[1];
-    __syncthreads();
     if (wave == 0) {
-        bool sel[2];
-        int rank[2];
-        uint32_t kmax = 0u;
+        float val[2];
+        uint32_t key[2], kv[2];
+        bool ok[2];
+        // Both logits of the lane in one round trip (branch-free loads).
+        const rsrc_t rl = make_rsrc(row, (uint32_t)E * 4u);
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
             const int e = lane + 64 * i;
-            rank[i] = 0;
-#pragma unroll
-            for (int w = 0; w < kT1Waves; ++w) rank[i] += r.prank[w][e];
-            sel[i] = e < E && rank[i] < topk;
-            if (sel[i] && rank[i] == 0) kmax = (uint32_t)(k64[i] >> 32);
+            val[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rl, e < E ? 4u * (uint32_t)e : kOob, 0, 0));
         }
-        kmax = wave_max_u32(kmax);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            ok[i] = lane + 64 * i < E;
+            key[i] = route_key(val[i]);
+            kv[i] = ok[i] ? key[i] : 0u;
+        }
+        int n = E;
+        uint32_t kmax;
+        const uint32_t thr = key_guess_threshold<2>(kv, ok, E, topk, topk + 16, n, kmax);
+        // Candidates (key >= thr) compacted in index order; zero entries up
+        // to a multiple of 4 (base <= E <= 128).
+        const uint64_t below_me = (1ull << lane) - 1ull;
+        uint64_t k64[2];
+        bool cand[2];
+        int base = 0;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            k64[i] = ((uint64_t)key[i] << 32) | (uint64_t)~(uint32_t)(lane + 64 * i);
+            cand[i] = ok[i] && key[i] >= thr;
+            const uint64_t m = __ballot(cand[i]);
+            if (cand[i]) r.key[base + __popcll(m & below_me)] = k64[i];
+            base += __popcll(m);
+        }
+        const int n4 = (base + 3) & ~3;
+        if (base + lane < n4) r.key[base + lane] = 0ull;
+        wave_lds_sync();
+        int rank[2] = {0, 0};
+        for (int j = 0; j < n4; j += 4) {
+            const uint64_t kj0 = r.key[j], kj1 = r.key[j + 1], kj2 = r.key[j + 2], kj3 = r.key[j + 3];
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                rank[i] += (kj0 > k64[i] ? 1 : 0) + (kj1 > k64[i] ? 1 : 0) + (kj2 > k64[i] ? 1 : 0) +
+                           (kj3 > k64[i] ? 1 : 0);
+        }
+        bool sel[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) sel[i] = cand[i] && rank[i] < topk;
         const float lmax = route_key_value(kmax);
         float ex[2];
         float psum = 0.0f;
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            const bool ok = lane + 64 * i < E;
-            ex[i] = ok ? expf(val[i] - lmax) : 0.0f;
-            if (renorm ? sel[i] : ok) psum += ex[i];
+            ex[i] = ok[i] ? expf(val[i] - lmax) : 0.0f;
+            if (renorm ? sel[i] : ok[i]) psum += ex[i];
         }
         psum = wave_sum_butterfly(psum);
 #pragma unroll

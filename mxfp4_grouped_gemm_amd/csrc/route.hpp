@@ -119,6 +119,49 @@ __device__ __forceinline__ void route_load(const float* __restrict__ row, int E,
     }
 }
 
+// Candidate threshold from one round of guesses, for up to 64 VPL keys (kv
+// and n as for key_threshold; ok: the slot holds an expert): 15 values
+// spread evenly between the token's smallest and largest logit, as keys
+// (lane c holds guess c), each counted with one ballot per slot. The largest
+// guess that at least need keys reach is a valid threshold; if none
+// qualifies, or more than stop keys reach the best one, the radix rounds of
+// key_threshold take over. One round of independent counts instead of ~5
+// dependent ones. kmax: the largest key (the token's first expert).
+template <int VPL>
+__device__ __forceinline__ uint32_t key_guess_threshold(const uint32_t (&kv)[VPL], const bool (&ok)[VPL], int E,
+                                                        int need, int stop, int& n, uint32_t& kmax) {
+    uint32_t hi = 0u, lo_inv = 0u;
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+        hi = kv[i] > hi ? kv[i] : hi;
+        const uint32_t inv = ok[i] ? ~kv[i] : 0u;
+        lo_inv = inv > lo_inv ? inv : lo_inv;
+    }
+    hi = wave_max_u32(hi);
+    const uint32_t lo = ~wave_max_u32(lo_inv);
+    kmax = hi;
+    const float vlo = route_key_value(lo), vhi = route_key_value(hi);
+    const uint32_t g = route_key(vlo + (vhi - vlo) * ((float)(threadIdx.x & 15) * 0.0625f));
+    uint32_t thr = 0u;
+    n = E;
+#pragma unroll
+    for (int c = 1; c < 16; ++c) {
+        const uint32_t t = (uint32_t)__builtin_amdgcn_readlane((int)g, c);
+        int cnt = 0;
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) cnt += __popcll(__builtin_amdgcn_ballot_w64(kv[i] >= t));
+        if (cnt >= need) {  // guesses rise with c: the last that qualifies is the largest
+            thr = t;
+            n = cnt;
+        }
+    }
+    if (n > stop) {
+        n = E;
+        thr = key_threshold<VPL, 2>(kv, need, stop, n);
+    }
+    return thr;
+}
+
 // Routes one token with one wave from its loaded logits (route_load).
 // Writes ids[rank] and weights[rank] for rank < topk (and ids_lds[rank] if
 // given). rk: this wave's LDS scratch of 64 * VPL entries (used only when
@@ -140,25 +183,25 @@ __device__ __forceinline__ void route_token_vals(const float (&val)[VPL], int E,
     uint32_t kmax = 0u;
     if constexpr (VPL <= 2) {
     // Up to 128 experts. First a threshold thr with at least topk keys >= thr
-    // (so every kept expert has key >= thr): two key bits per round, as in
-    // the radix select below, but stopping once at most topk + 16 keys reach
-    // it (N(0,1) logits: ~5 rounds leave ~20 of 112). Only those candidates are
+    // (so every kept expert has key >= thr) and few more: the best of 15
+    // guesses between the smallest and largest logit (N(0,1) logits: ~20 of
+    // 112 reach it), else radix rounds of two key bits, as in the radix
+    // select below, stopping once at most topk + 16 keys reach it. Only those candidates are
     // then ranked exactly: each lane compares its (key, ~index) against the
     // candidates' entries, compacted into wave-private LDS (broadcast reads);
     // a candidate's rank among them is its rank among all experts, since
     // every other expert has a smaller key. No scalar chains beyond the
     // rounds, and the compare count is the candidates', not E. In the fused
-    // route + align kernel (16 waves routing on one CU) the routing phase
-    // went from 5.6 to 3.8-4.2 us at 16 tokens of 112 experts and from 10 to
-    // 6-7 us at 32 tokens. Four key bits a round (15 compares per slot) took
-    // longer than two, and neither beats the four-wave split count of the
-    // one-token kernel (route_gate_up_t1_kernel), whose rounds are latency
-    // bound.
+    // route + align kernel (16 waves routing on one CU) the kernel went from
+    // 8.9 to 6.7 us at 16 tokens of 112 experts and from 13.9 to 10.0 us at
+    // 32 with the radix rounds alone (~190 ns each, latency-bound), to 6.2
+    // and 9.2 us with the guesses first. Four key bits a round (15 compares
+    // per slot) took longer than two.
     uint32_t kv[VPL];
 #pragma unroll
     for (int i = 0; i < VPL; ++i) kv[i] = ok[i] ? key[i] : 0u;
     int n = E;
-    const uint32_t thr = key_threshold<VPL, 2>(kv, topk, topk + 16, n);
+    const uint32_t thr = key_guess_threshold<VPL>(kv, ok, E, topk, topk + 16, n, kmax);
     uint64_t* kk = rk;
     uint64_t k64[VPL];
     bool cand[VPL];
@@ -188,11 +231,7 @@ __device__ __forceinline__ void route_token_vals(const float (&val)[VPL], int E,
     }
     wave_lds_sync();  // the next token's entries overwrite this wave's scratch
 #pragma unroll
-    for (int i = 0; i < VPL; ++i) {
-        sel[i] = cand[i] && rank[i] < topk;
-        if (sel[i] && rank[i] == 0) kmax = key[i];
-    }
-    kmax = wave_max_u32(kmax);
+    for (int i = 0; i < VPL; ++i) sel[i] = cand[i] && rank[i] < topk;
     } else {
     // k-th largest key: the largest T with count(key >= T) >= topk, two key
     // bits per round (three independent counts). Slots past E get key 0,
