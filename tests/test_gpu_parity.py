@@ -224,14 +224,33 @@ def test_route_align_small_matches_oracle(moe, T, E, topk, bm):
                                                 (640, 7, False, True), (512, 15, True, False),
                                                 (129, 15, True, False), (200, 64, True, True),
                                                 (256, 8, False, False), (1024, 64, False, True),
-                                                (300, 300 // 5, True, True), (130, 130 - 66, False, False)])
+                                                (300, 300 // 5, True, True), (130, 130 - 66, False, False),
+                                                (896, 15, True, "dup"), (1024, 40, False, "dup"),
+                                                (896, 8, True, "inf"), (700, 12, True, "spread")])
 def test_route_align_one_token_many_experts(moe, E, topk, renorm, ties):
     """One token over 129-1024 experts is routed by a whole workgroup (a
-    radix select over 8-bit digits): ids and weights equal the oracle's, and
+    64-bin histogram between the smallest and largest logit, else a radix
+    select over 8-bit digits): ids and weights equal the oracle's, and
     route_align's equal moe_route_topk's bit for bit; the align/sort outputs
-    equal the oracle's."""
+    equal the oracle's. "dup": the k-th largest logit copied to lower and
+    higher experts (ties at the threshold among few candidates); "inf":
+    extremes whose difference overflows (no histogram); "spread": one huge
+    logit (every other key in the lowest bin: the radix select)."""
     rng = np.random.default_rng(E + topk)
-    if ties:
+    if ties == "dup":
+        logits = rng.standard_normal((1, E)).astype(np.float32) * 2
+        order = np.argsort(-logits[0], kind="stable")
+        kth = logits[0, order[topk - 1]]
+        logits[0, order[topk + 3:topk + 7]] = kth  # four more at the threshold
+        logits[0, 0] = kth
+    elif ties == "inf":
+        logits = rng.standard_normal((1, E)).astype(np.float32)
+        logits[0, E // 3] = np.float32(3e38)
+        logits[0, E // 2] = np.float32(-3e38)
+    elif ties == "spread":
+        logits = rng.standard_normal((1, E)).astype(np.float32)
+        logits[0, 5] = np.float32(1e30)
+    elif ties:
         logits = rng.integers(-3, 4, size=(1, E)).astype(np.float32)
     else:
         logits = rng.standard_normal((1, E)).astype(np.float32) * 2
