@@ -5,13 +5,12 @@
 // topk (equal logits: lower index first), weight them by their softmax
 // probabilities, renormalised over the kept experts on request.
 //
-// Up to 128 experts, a few radix rounds (below) find a key threshold that
-// at least topk and only a few more experts reach; every lane then ranks its
-// candidates directly: it counts the candidates ordered before each of them
-// (larger key, or equal key and lower index) against their keys in the
-// wave's LDS scratch, and keeps those ranked below topk (at 16 tokens of 112
-// experts, four routing waves per SIMD: 2.5 -> 0.8 us for the routing
-// phase against counting over all experts). For more experts, selection is a radix select over
+// Up to 128 experts, one round of guesses (else a few radix rounds) finds a
+// key threshold that at least topk and only a few more experts reach; every
+// lane then ranks its candidates directly: it counts the candidates ordered
+// before each of them (larger key, or equal key and lower index) against
+// their keys in the wave's LDS scratch, and keeps those ranked below topk.
+// For more experts, selection is a radix select over
 // order-preserving 32-bit keys: 16 rounds of (compare, ballot, popcount) over
 // two key bits find the k-th largest key; keys above it are kept and the
 // ties at it are taken lowest index first; the kept experts are then ranked
@@ -186,10 +185,11 @@ __device__ __forceinline__ void route_token_vals(const float (&val)[VPL], int E,
     // (so every kept expert has key >= thr) and few more: the best of 15
     // guesses between the smallest and largest logit (N(0,1) logits: ~20 of
     // 112 reach it), else radix rounds of two key bits, as in the radix
-    // select below, stopping once at most topk + 16 keys reach it. Only those candidates are
-    // then ranked exactly: each lane compares its (key, ~index) against the
-    // candidates' entries, compacted into wave-private LDS (broadcast reads);
-    // a candidate's rank among them is its rank among all experts, since
+    // select below, stopping once at most topk + 16 keys reach it. Only
+    // those candidates are then ranked exactly: each lane compares its
+    // (key, ~index) against the candidates' entries, compacted into
+    // wave-private LDS (broadcast reads); a candidate's rank among them is
+    // its rank among all experts, since
     // every other expert has a smaller key. No scalar chains beyond the
     // rounds, and the compare count is the candidates', not E. In the fused
     // route + align kernel (16 waves routing on one CU) the kernel went from
