@@ -116,13 +116,21 @@ def test_route_matches_oracle(moe, name, _):
                                                   (33, 1, 1, True, False), (4, 112, 15, False, False),
                                                   (8, 112, 15, True, True), (5, 128, 40, False, True),
                                                   (4, 128, 64, True, True), (6, 112, 15, True, "zeros"),
-                                                  (3, 97, 1, True, False), (7, 120, 48, True, True)])
+                                                  (3, 97, 1, True, False), (7, 120, 48, True, True),
+                                                  (5, 112, 15, True, "dup"), (9, 128, 8, False, "dup")])
 def test_route_edge_cases(moe, T, E, topk, renorm, ties):
     """Ties at the top-k boundary (integer logits), the candidate threshold
     at up to 128 experts with few and with many candidates, and +0 / -0 logits
     (equal keys: lower index first)."""
     rng = np.random.default_rng(T * 7 + E)
-    if ties == "zeros":
+    if ties == "dup":  # the k-th largest copied to four lower-ranked experts and expert 0
+        logits = rng.standard_normal((T, E)).astype(np.float32)
+        for t in range(T):
+            order = np.argsort(-logits[t], kind="stable")
+            kth = logits[t, order[topk - 1]]
+            logits[t, order[topk:topk + 4]] = kth
+            logits[t, 0] = kth
+    elif ties == "zeros":
         logits = rng.integers(-1, 2, size=(T, E)).astype(np.float32)
         logits[rng.random((T, E)) < 0.5] *= np.float32(0.0)   # signed zeros from -1 and +1
         logits[rng.random((T, E)) < 0.3] = np.float32(-0.0)
@@ -700,15 +708,25 @@ def test_forward_monolithic(moe, T, H, I, E, topk, bm, renorm, bias):
     check_close(out_f64(bufs.out), ref, f"monolithic T={T} H={H} I={I} E={E} k={topk} bm={bm} renorm={renorm} bias={bias}")
 
 
-@pytest.mark.parametrize("E,topk", [(112, 15), (300, 20), (1024, 64)])
-def test_forward_monolithic_tied_logits(moe, E, topk):
-    """One token whose logits take a few values only (many ties, broken by
-    the lower index): the monolithic call (routing inside gate_up up to 128
+@pytest.mark.parametrize("E,topk,mode", [(112, 15, "halves"), (300, 20, "halves"), (1024, 64, "halves"),
+                                         (112, 15, "dup"), (128, 8, "dup"), (64, 64, "dup")])
+def test_forward_monolithic_tied_logits(moe, E, topk, mode):
+    """One token whose logits take a few values only ("halves": many ties,
+    broken by the lower index) or are continuous with the k-th largest
+    copied to five more experts ("dup": ties at the threshold among few
+    candidates): the monolithic call (routing inside gate_up up to 128
     experts, the one-token routing kernel above) gives the standalone
     routing's ids, weights and align/sort arrays bit for bit, and the
     oracle's ids."""
     wl = synth.small(T=1, H=512, I=256, E=E, topk=topk, seed=E + topk, scale_lo=118, scale_hi=128)
-    logits = np.round(wl.logits * 2.0).astype(np.float32) / 2.0
+    if mode == "halves":
+        logits = np.round(wl.logits * 2.0).astype(np.float32) / 2.0
+    else:
+        logits = wl.logits.astype(np.float32).copy()
+        order = np.argsort(-logits[0], kind="stable")
+        kth = logits[0, order[topk - 1]]
+        logits[0, order[topk:topk + 4]] = kth
+        logits[0, 0] = kth
     w = weights_dev(wl)
     lg = dev(logits)
     bufs = moe.moe_a16w4_forward_monolithic(x_dev(wl), lg, *w, topk)
@@ -721,7 +739,7 @@ def test_forward_monolithic_tied_logits(moe, E, topk):
     rids, rw = oracle.route_topk(logits, topk, renormalize=True)
     assert np.array_equal(bufs.ids.cpu().numpy().reshape(rids.shape), rids)
     ref = oracle.moe_forward(wl.x, wl.w13, wl.w13_scale, wl.w2, wl.w2_scale, 0, rids, rw, I=256)
-    check_close(out_f64(bufs.out), ref, f"monolithic tied logits E={E} k={topk}")
+    check_close(out_f64(bufs.out), ref, f"monolithic tied logits ({mode}) E={E} k={topk}")
 
 
 def test_forward_monolithic_stages_and_replay(moe):
