@@ -28,6 +28,20 @@
 
 namespace moe {
 
+// Inclusive prefix sum over the 64 lanes of a wave (all active), by DPP
+// instead of six LDS permutes: row shifts by 1, 2, 4 and 8 scan each 16-lane
+// row (lanes shifted in from outside the row add 0), then lane 15's total
+// is broadcast into rows 1 and 3 and lane 31's into rows 2 and 3.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);  // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);  // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);  // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);  // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15 into rows 1, 3
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31 into rows 2, 3
+    return v;
+}
+
 constexpr int kSortThreads = 1024;
 constexpr int kSortWaves = kSortThreads / 64;
 constexpr int kMaxExperts = 1024;
@@ -184,14 +198,9 @@ __device__ __forceinline__ void align_sort_body(SortShared& sh, const int32_t* i
             const int e = base + lane;
             const int c = e < E ? sh.counts[e] : 0;
             const int padded = (c + bm - 1) / bm * bm;
-            int incl = padded;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const int o = __shfl_up(incl, off);
-                if (lane >= off) incl += o;
-            }
+            const int incl = wave_incl_scan(padded);
             if (e < E) sh.offs[e] = carry + incl - padded;
-            carry += __shfl(incl, 63);
+            carry += __builtin_amdgcn_readlane(incl, 63);
         }
         if (lane == 0) sh.offs[E] = carry;
     }
@@ -341,13 +350,9 @@ __global__ __launch_bounds__(NW * 64) void route_align_small_kernel(
             pad[c] = (len + bm - 1) & -bm;  // block_m is a power of two
             local += pad[c];
         }
-        int incl = local;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const int o = __shfl_up(incl, off);
-            if (lane >= off) incl += o;
-        }
-        const int total = __shfl(incl, 63);
+        const int incl = wave_incl_scan(local);
+        const int total = __builtin_amdgcn_readlane(incl, 63);
+        const int lgbm = __builtin_ctz((unsigned)bm);
         int base = incl - local;
 #pragma unroll
         for (int c = 0; c < VPL; ++c) {
@@ -355,7 +360,7 @@ __global__ __launch_bounds__(NW * 64) void route_align_small_kernel(
             if (x < E) {
                 expert_offsets[x] = base;
                 start[x] = base;
-                for (int b = base / bm; b < (base + pad[c]) / bm; ++b) blk[b] = x;
+                for (int b = base >> lgbm; b < (base + pad[c]) >> lgbm; ++b) blk[b] = x;
             }
             base += pad[c];
         }
