@@ -28,20 +28,6 @@
 
 namespace moe {
 
-// Inclusive prefix sum over the 64 lanes of a wave (all active), by DPP
-// instead of six LDS permutes: row shifts by 1, 2, 4 and 8 scan each 16-lane
-// row (lanes shifted in from outside the row add 0), then lane 15's total
-// is broadcast into rows 1 and 3 and lane 31's into rows 2 and 3.
-__device__ __forceinline__ int wave_incl_scan(int v) {
-    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);  // row_shr:1
-    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);  // row_shr:2
-    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);  // row_shr:4
-    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);  // row_shr:8
-    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15 into rows 1, 3
-    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31 into rows 2, 3
-    return v;
-}
-
 constexpr int kSortThreads = 1024;
 constexpr int kSortWaves = kSortThreads / 64;
 constexpr int kMaxExperts = 1024;

@@ -161,6 +161,20 @@ __device__ __forceinline__ uint32_t key_guess_threshold(const uint32_t (&kv)[VPL
     return thr;
 }
 
+// Inclusive prefix sum over the 64 lanes of a wave (all active), by DPP
+// instead of six LDS permutes: row shifts by 1, 2, 4 and 8 scan each 16-lane
+// row (lanes shifted in from outside the row add 0), then lane 15's total
+// is broadcast into rows 1 and 3 and lane 31's into rows 2 and 3.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);  // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);  // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);  // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);  // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15 into rows 1, 3
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31 into rows 2, 3
+    return v;
+}
+
 // Routes one token with one wave from its loaded logits (route_load).
 // Writes ids[rank] and weights[rank] for rank < topk (and ids_lds[rank] if
 // given). rk: this wave's LDS scratch of 64 * VPL entries (used only when

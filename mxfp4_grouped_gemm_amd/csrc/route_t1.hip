@@ -90,12 +90,7 @@ __global__ __launch_bounds__(kT1RouteThreads) void route_one_token_kernel(
     if (wave == 0) {
         // Lane l holds bin 63 - l; inclusive counts from the top.
         const uint32_t c = hist[63 - lane];
-        uint32_t incl = c;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const uint32_t o = __shfl_up(incl, off);
-            if (lane >= off) incl += o;
-        }
+        const uint32_t incl = (uint32_t)wave_incl_scan((int)c);
         const uint64_t reach = __ballot(incl >= (uint32_t)topk);
         const int l = reach ? __ffsll((unsigned long long)reach) - 1 : 63;
         if (lane == 0) {
@@ -146,12 +141,7 @@ __global__ __launch_bounds__(kT1RouteThreads) void route_one_token_kernel(
                 c[q] = hist[255 - 4 * lane - q];
                 local += c[q];
             }
-            uint32_t incl = local;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const uint32_t o = __shfl_up(incl, off);
-                if (lane >= off) incl += o;
-            }
+            const uint32_t incl = (uint32_t)wave_incl_scan((int)local);
             const uint32_t excl = incl - local;
             if (excl < (uint32_t)need && (uint32_t)need <= incl) {  // exactly one lane
                 uint32_t before = excl;
