@@ -33,6 +33,7 @@
 // (64 bytes apart) per 16 lanes; with K a multiple of 512 both the fill and
 // the operand reads touch each of the 64 banks once per 16 lanes.
 #include "gemv_mfma.hpp"
+#include "route.hpp"  // wave_incl_scan
 
 namespace moe {
 
@@ -103,12 +104,7 @@ void gemv_resident_kernel(MoeGemmArgs a) {
             for (int i = 0; i < 4; ++i) cnt += ((int)sid[k][i] >= 0 && (int)sid[k][i] < P) ? 1 : 0;
         bexp_lds[tid] = bexp_t;
         const uint32_t cost = !mine ? 0u : cnt > 8 ? (kInt4 ? 28u : 19u) : cnt > 4 ? 14u : 13u;
-        uint32_t incl = cost;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const uint32_t t = __shfl_up(incl, off);
-            if (lane >= off) incl += t;
-        }
+        uint32_t incl = (uint32_t)wave_incl_scan((int)cost);
         if (lane == 63) wsum[wave] = incl;
         if (tid == 0) bound[0] = bound[1] = S;
         __syncthreads();
@@ -119,11 +115,14 @@ void gemv_resident_kernel(MoeGemmArgs a) {
             incl += w < wave ? ws : 0u;
             total += ws;
         }
-        const uint64_t tt = (uint64_t)total * (uint64_t)spb;
-        const uint64_t lo = (uint64_t)(incl - cost) * spb, hi = (uint64_t)incl * spb;
+        // 32-bit: total <= 512 blocks x 28, spb <= 64 (H, I <= 4096) and a
+        // grid of at most 4096 workgroups (the launcher's bound) keep every
+        // product below 2^32.
+        const uint32_t tt = total * (uint32_t)spb;
+        const uint32_t lo = (incl - cost) * (uint32_t)spb, hi = incl * (uint32_t)spb;
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-            const uint64_t t = (uint64_t)(blockIdx.x + j) * tt / gridDim.x;
+            const uint32_t t = (blockIdx.x + (uint32_t)j) * tt / gridDim.x;
             if (mine && t >= lo && t < hi) bound[j] = (int64_t)tid * spb + (int64_t)((t - lo) / cost);
         }
         __syncthreads();
@@ -464,7 +463,7 @@ static int resident_grid() {
 bool gemv_resident_eligible(const MoeGemmArgs& a) {
     const int kmax = a.fmt == kFmtMxfp4 ? 4096 : 3584;
     return (a.fmt == kFmtMxfp4 || a.fmt == kFmtInt4g32) && a.bm == 16 && a.cap / 16 <= kPxMaxBlocks &&
-           resident_grid() >= 32 && a.H <= kmax && a.I <= kmax && a.H % 512 == 0 && a.I % 512 == 0 &&
+           resident_grid() >= 32 && resident_grid() <= 4096 && a.H <= kmax && a.I <= kmax && a.H % 512 == 0 && a.I % 512 == 0 &&
            (int64_t)a.T * a.topk * a.I * 2 < 0x7fff0000LL && (int64_t)a.T * a.H * 2 < 0x7fff0000LL;
 }
 
